@@ -1,0 +1,638 @@
+"""Plain CPU oracle of the EAGLE-3 draft-and-verify hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg; nothing on the product path imports it.  It
+shares no code with the HIP library.
+
+Everything is NumPy float64.  A value that the method stores is rounded at the
+storage point: float64 -> float32 -> (bf16 when the drafter runs in bf16).
+Logits, log-sum-exp, log-probabilities and tree scores are float32 values.
+
+Sources (web pages; cited by title and section):
+  [E3]  "EAGLE-3: Scaling up Inference Acceleration of Large Language Models
+        via Training-Time Test" (paper summary page), sections 3.2 Big-Picture
+        Architecture, 3.4 "Feature Extraction: What Changes from EAGLE to
+        EAGLE-3", "The Draft Model Architecture in Detail", "The Inference
+        Pipeline: Drafting and Verification", 6 Limitation 6 (LLaMA family:
+        pre-normalisation, SwiGLU, rotary embeddings, GQA).
+  [E1]  "EAGLE: Speculative Sampling Requires Rethinking Feature Uncertainty"
+        (paper summary page), 3.4 "Tree-Structured Draft Generation",
+        "Verification Phase: Multi-Round Speculative Sampling on Trees"
+        (Algorithm 1), "The Full Inference Loop".
+  [M75] "M7.5 - EAGLE Feature Drafting: Uncertainty, Dynamic Trees, HASS, and
+        EAGLE-3", sections 0x05A-0x05D, 0x06A-0x06C, 0x08B, 0x08C, 0x09.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * fusion and input FCs carry no bias; LM head has no bias;
+  * the draft layer is a LLaMA pre-norm block: RMSNorm (eps 1e-5) -> attention
+    with rotate-half RoPE -> residual -> RMSNorm -> SwiGLU -> residual; a final
+    RMSNorm with its own gain precedes the LM head; the un-normed output `a`
+    is the state fed to children;
+  * draft confidences are softmax of raw logits (temperature 1);
+  * node ids follow creation order with children of one parent created in
+    ascending token id, parents taken in ascending node id (only exact score
+    ties see this order);
+  * verification of deterministic top-k children uses Algorithm 1 with point
+    mass proposals; children are tested in ascending token id; the residual
+    draw is an inverse CDF over ascending token id.
+
+Parity pins for every function live in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "LOG_EPS", "bf16_round", "store", "Weights", "rmsnorm", "rope", "silu",
+    "fuse", "layer", "topk_desc", "lse32", "child_logprob", "DraftKV",
+    "draft_tree", "select_key", "eagle2_tree", "flatten", "verify", "verify_row",
+    "commit", "decision_margin", "score_rows", "causal_attention", "attend",
+]
+
+# log of the confidence floor 1e-12 used for ranking ([M75] 0x06A), float32
+LOG_EPS = float(np.float32(math.log(1e-12)))
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+def bf16_round(x) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16, ties to even.
+
+    bfloat16 keeps the top 16 bits of an IEEE float32.  Rounding adds half of
+    the dropped range (0x7FFF) plus the lowest kept bit, then truncates.
+    NaN stays NaN (quiet bit forced)."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    nan = np.isnan(x32)
+    if nan.any():
+        r = np.where(nan, (x32.view(np.uint32) | 0x00400000) & 0xFFFF0000, r)
+    return r.view(np.float32).reshape(x32.shape)
+
+
+def store(x, dtype: str) -> np.ndarray:
+    """Value of `x` after it is stored in the drafter's storage type."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "bf16":
+        x32 = bf16_round(x32)
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return x32.astype(np.float64)
+
+
+class Weights:
+    """Drafter weights as float64 copies of the stored values."""
+
+    NAMES = ("w_fuse", "w_in", "embed", "wq", "wk", "wv", "wo", "w_gate",
+             "w_up", "w_down", "w_lm", "g_attn", "g_mlp", "g_final")
+
+    def __init__(self, cfg, arrays: dict):
+        self.cfg = cfg
+        for n in self.NAMES:
+            setattr(self, n, store(arrays[n], cfg.dtype))
+
+
+# ---------------------------------------------------------------------------
+# elementwise pieces of the draft layer
+# ---------------------------------------------------------------------------
+def rmsnorm(x, gain, eps: float, dtype: str) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * gain, stored ([E3] Limitation 6: the
+    LLaMA family uses pre-normalisation; RMSNorm is its norm)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return store(x / np.sqrt(ms + eps) * gain, dtype)
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotate-half rotary embedding of the last axis (pairs i, i + hd/2).
+
+    Angle of pair i at position p is p * theta^(-2i/hd), in float64; cos and
+    sin are then rounded to float32.  `x` is [..., hd], `pos` broadcasts over
+    the leading axes.  Result is unrounded float64."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    half = hd // 2
+    i = np.arange(half, dtype=np.float64)
+    inv = theta ** (-(2.0 * i) / hd)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c = np.cos(ang).astype(np.float32).astype(np.float64)
+    s = np.sin(ang).astype(np.float32).astype(np.float64)
+    while c.ndim < x.ndim:
+        c = c[..., None, :]
+        s = s[..., None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+# ---------------------------------------------------------------------------
+# (1) multi-layer feature fusion
+# ---------------------------------------------------------------------------
+def fuse(W: Weights, low, mid, high) -> np.ndarray:
+    """g = W_R [l; m; h] for each row ([E3] "Change 2: The fusion FC layer";
+    [M75] 0x08B): concat of the three k-dim taps, projected 3k -> k."""
+    cat = np.concatenate([np.atleast_2d(low), np.atleast_2d(mid),
+                          np.atleast_2d(high)], axis=-1).astype(np.float64)
+    return store(cat @ W.w_fuse.T, W.cfg.dtype)
+
+
+# ---------------------------------------------------------------------------
+# attention over a visible key set
+# ---------------------------------------------------------------------------
+def attend(q, keys, vals) -> np.ndarray:
+    """softmax(q k^T / sqrt(hd)) v for one query vector, float64."""
+    s = keys @ q / math.sqrt(q.shape[-1])
+    s = s - s.max()
+    p = np.exp(s)
+    p /= p.sum()
+    return p @ vals
+
+
+def causal_attention(q, k, v) -> np.ndarray:
+    """Plain causal attention over a chain: row i sees rows 0..i."""
+    out = np.zeros_like(q, dtype=np.float64)
+    for i in range(q.shape[0]):
+        out[i] = attend(q[i], k[: i + 1], v[: i + 1])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (2) one draft step: join + single decoder layer + LM head
+# ---------------------------------------------------------------------------
+class DraftKV:
+    """One sequence's draft KV cache, [n_kv, cap, hd] float64 (stored values)."""
+
+    def __init__(self, k, v):
+        self.k = np.array(k, dtype=np.float64)
+        self.v = np.array(v, dtype=np.float64)
+
+    def copy(self):
+        return DraftKV(self.k, self.v)
+
+
+def layer(W: Weights, kv: DraftKV, src, tok, pos, dest, visible):
+    """One draft pass over R query rows of one sequence.
+
+    src [R,H]: fused target feature g (seed rows) or the parent's draft state a
+    (tree rows) -- [E3] "The Draft Model Architecture in Detail" (input_i =
+    [g_i; e_i], projected by a second FC) and "The Inference Pipeline" (a
+    stands in for g at drafted positions); [M75] 0x08B u_t = W_I[r_t; e(x)].
+    tok [R]: token whose embedding joins the row.  pos [R]: RoPE position.
+    dest [R]: cache index receiving the row's K/V.  visible[r]: cache indices
+    row r attends to ([M75] 0x08C: target prefix, draft ancestors, itself).
+
+    Returns dict with x, q, k, v, o, h, t, a (stored values) and fp32 logits.
+    """
+    cfg = W.cfg
+    dt, eps = cfg.dtype, cfg.eps
+    src = np.atleast_2d(np.asarray(src, dtype=np.float64))
+    tok = np.asarray(tok, dtype=np.int64)
+    R = src.shape[0]
+    nq, nkv, hd = cfg.n_q, cfg.n_kv, cfg.hd
+    group = nq // nkv
+
+    x = store(np.concatenate([src, W.embed[tok]], axis=1) @ W.w_in.T, dt)
+    n1 = rmsnorm(x, W.g_attn, eps, dt)
+    q = rope((n1 @ W.wq.T).reshape(R, nq, hd), pos, cfg.theta)
+    k = rope((n1 @ W.wk.T).reshape(R, nkv, hd), pos, cfg.theta)
+    v = (n1 @ W.wv.T).reshape(R, nkv, hd)
+    q, k, v = store(q, dt), store(k, dt), store(v, dt)
+    for r in range(R):
+        kv.k[:, dest[r]] = k[r]
+        kv.v[:, dest[r]] = v[r]
+    o = np.zeros((R, nq, hd))
+    for r in range(R):
+        idx = np.asarray(visible[r], dtype=np.int64)
+        for hh in range(nq):
+            g = hh // group
+            o[r, hh] = attend(q[r, hh], kv.k[g, idx], kv.v[g, idx])
+    o = store(o, dt)
+    h = store(x + o.reshape(R, nq * hd) @ W.wo.T, dt)
+    n2 = rmsnorm(h, W.g_mlp, eps, dt)
+    t = store(silu(n2 @ W.w_gate.T) * (n2 @ W.w_up.T), dt)
+    a = store(h + t @ W.w_down.T, dt)
+    nf = rmsnorm(a, W.g_final, eps, dt)
+    logits = (nf @ W.w_lm.T).astype(np.float32)
+    return {"x": x, "q": q, "k": k, "v": v, "o": o, "h": h, "t": t, "a": a,
+            "logits": logits}
+
+
+def topk_desc(logits, K: int) -> np.ndarray:
+    """Ids of the K largest logits ordered by (-logit, id)."""
+    lg = np.asarray(logits)
+    order = np.lexsort((np.arange(lg.shape[-1]), -lg.astype(np.float64)))
+    return order[:K]
+
+
+def lse32(logits) -> np.float32:
+    """log-sum-exp of one float32 logit row, computed in float64, as float32."""
+    lg = np.asarray(logits, dtype=np.float64)
+    m = lg.max()
+    return np.float32(m + math.log(np.exp(lg - m).sum()))
+
+
+def child_logprob(logit, lse) -> np.float32:
+    """log(max(confidence, 1e-12)) of a child in float32 ([M75] 0x06A)."""
+    lp = np.float32(np.float32(logit) - np.float32(lse))
+    return np.float32(max(lp, np.float32(LOG_EPS)))
+
+
+# ---------------------------------------------------------------------------
+# (3) EAGLE-2 dynamic tree
+# ---------------------------------------------------------------------------
+def select_key(node):
+    """Global order of [M75] 0x06B: higher value first, shallower, older."""
+    return (-float(node["score"]), node["depth"], node["id"])
+
+
+def eagle2_tree(root, expand, width: int, max_depth: int, budget: int):
+    """EAGLE-2 expansion and reranking ([M75] 0x06A-0x06B).
+
+    `root` is the seed node (depth 0, log value 0).  `expand(parents, depth)`
+    returns, for each parent (given in ascending node id), its children as
+    (token, log_confidence) pairs; log_confidence is float32 log p.  The value
+    of a node is the float32 sum of log(max(confidence, 1e-12)) along its path.
+    Each depth expands the `width` best nodes of the newest layer under the
+    order (-value, depth, node id); after `max_depth` expansions the `budget`
+    best nodes overall are returned.  Node ids follow creation order.
+
+    Raises ValueError on the argument and record violations the pages list:
+    width < 1, negative budget or depth, a confidence outside [0, 1], a
+    repeated token under one parent, sibling mass above one (tolerance 1e-5:
+    confidences arrive as float32 logs).  Returns (selected, all_nodes)."""
+    if type(width) is not int or width < 1:
+        raise ValueError("expansion width must be a positive integer")
+    for val in (budget, max_depth):
+        if type(val) is not int or val < 0:
+            raise ValueError("budget and depth must be nonnegative integers")
+    nodes = []
+    if budget == 0:
+        return [], nodes
+    frontier = [root]
+    for depth in range(max_depth):
+        if not frontier:
+            break
+        chosen = sorted(frontier, key=select_key)[:width]
+        chosen.sort(key=lambda n: n["id"])
+        kids = expand(chosen, depth)
+        nxt = []
+        for p, plist in zip(chosen, kids):
+            seen, mass = set(), 0.0
+            for tok, lc in plist:
+                lc = np.float32(lc)
+                conf = math.exp(float(lc))
+                if not math.isfinite(float(lc)) and float(lc) != -math.inf:
+                    raise ValueError("confidence must be a finite probability")
+                if not 0.0 <= conf <= 1.0 + 1e-6:
+                    raise ValueError("confidence must be a finite probability")
+                if tok in seen:
+                    raise ValueError("duplicate token under one parent")
+                seen.add(tok)
+                mass += conf
+                if mass > 1.0 + 1e-5:
+                    raise ValueError("sibling probability mass exceeds one")
+                c = {"id": len(nodes), "token": tok, "parent": p,
+                     "depth": p["depth"] + 1,
+                     "score": np.float32(p["score"]
+                                         + max(lc, np.float32(LOG_EPS))),
+                     "slot": -1}
+                nodes.append(c)
+                nxt.append(c)
+        frontier = nxt
+    selected = sorted(nodes, key=select_key)[:budget]
+    return selected, nodes
+
+
+def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
+               record: bool = False):
+    """Draft one tree for one sequence.
+
+    Seed rows ([M75] 0x05A: [f_t, embed(x_{t+1})]) are appended to the draft
+    KV at cache indices len_in.. and processed causally; the last seed row is
+    the root.  Then EAGLE-2 growth (eagle2_tree) with width K, depth D and
+    budget N, where expanding a node runs one draft pass over it and takes its
+    top-K tokens as children (log confidence = logit - lse, float32).  Nodes
+    expanded at depth d >= 1 get scratch slot (d-1)*K + rank (rank in
+    ascending node id) at cache index len_out + slot, position P_root + d, and
+    see the committed prefix, their ancestors' slots and their own slot.
+
+    Mutates kv (seed rows + scratch rows).  Returns (tree, info)."""
+    cfg = W.cfg
+    K, D, N = cfg.K, cfg.D, cfg.N
+    seed_src = np.atleast_2d(np.asarray(seed_src, dtype=np.float64))
+    seed_tok = np.asarray(seed_tok, dtype=np.int64)
+    s = len(seed_tok)
+    len_out = len_in + s
+    p_root = len_out - 1
+    info = {"passes": [], "len_out": len_out, "nodes": []}
+
+    out = layer(W, kv, seed_src, seed_tok,
+                pos=np.arange(len_in, len_out), dest=np.arange(len_in, len_out),
+                visible=[np.arange(0, len_in + i + 1) for i in range(s)])
+    root = {"id": -1, "token": int(seed_tok[-1]), "parent": None, "depth": 0,
+            "score": np.float32(0.0), "slot": -1, "a": out["a"][-1],
+            "logits": out["logits"][-1], "mask_slots": []}
+    info["root"] = root
+    if record:
+        info["passes"].append({"rows": [root], "out": out})
+
+    def children(parents):
+        res = []
+        for p in parents:
+            lg = p["logits"]
+            lse = lse32(lg)
+            res.append([(int(t), child_logprob(lg[t], lse))
+                        for t in sorted(int(i) for i in topk_desc(lg, K))])
+        return res
+
+    def expand(chosen, depth):
+        if depth == 0:
+            return children(chosen)
+        for r, n in enumerate(chosen):
+            n["slot"] = (depth - 1) * K + r
+            n["mask_slots"] = n["parent"]["mask_slots"] + [n["slot"]]
+        vis = [np.concatenate([np.arange(len_out),
+                               len_out + np.asarray(n["mask_slots"])])
+               for n in chosen]
+        o = layer(W, kv, np.stack([n["parent"]["a"] for n in chosen]),
+                  [n["token"] for n in chosen],
+                  pos=np.full(len(chosen), p_root + depth),
+                  dest=np.array([len_out + n["slot"] for n in chosen]),
+                  visible=vis)
+        for r, n in enumerate(chosen):
+            n["a"] = o["a"][r]
+            n["logits"] = o["logits"][r]
+        if record:
+            info["passes"].append({"rows": chosen, "out": o})
+        return children(chosen)
+
+    selected, nodes = eagle2_tree(root, expand, K, D, N)
+    for n in selected:
+        n["selected"] = True
+    info["nodes"] = nodes
+    return flatten(cfg, root, selected, p_root), info
+
+
+def flatten(cfg, root, selected, p_root):
+    """Flattened tree ([M75] 0x05C, 0x09: rows, positions, ancestry mask,
+    retrieve map).  Row 0 is the root; rows 1..n are the selected nodes in
+    ascending node id, i.e. by (depth, parent row, token id).  Arrays have
+    N+1 rows; unused rows hold -1 (0 for score, n_child, mask)."""
+    N = cfg.N
+    W = (N + 1 + 63) // 64
+    sel = sorted(selected, key=lambda n: n["id"])
+    row_of = {id(root): 0}
+    for r, n in enumerate(sel):
+        row_of[id(n)] = r + 1
+    n_rows = N + 1
+    t = {k: np.full(n_rows, -1, dtype=np.int32) for k in
+         ("token", "parent", "depth", "position", "kv_slot", "first_child")}
+    t["n_child"] = np.zeros(n_rows, dtype=np.int32)
+    t["score"] = np.zeros(n_rows, dtype=np.float32)
+    t["mask"] = np.zeros((n_rows, W), dtype=np.uint64)
+    t["n_nodes"] = len(sel)
+    rows = [root] + sel
+    for r, n in enumerate(rows):
+        t["token"][r] = n["token"]
+        t["parent"][r] = -1 if n["parent"] is None else row_of[id(n["parent"])]
+        t["depth"][r] = n["depth"]
+        t["position"][r] = p_root + n["depth"]
+        t["kv_slot"][r] = n["slot"]
+        t["score"][r] = n["score"]
+        a = r
+        while a != -1:
+            t["mask"][r, a // 64] |= np.uint64(1) << np.uint64(a % 64)
+            a = t["parent"][a]
+    for r in range(1, len(rows)):
+        p = t["parent"][r]
+        if t["n_child"][p] == 0:
+            t["first_child"][p] = r
+        t["n_child"][p] += 1
+    return t
+
+
+def score_rows(W: Weights, kv: DraftKV, tree, info):
+    """Draft logits at every flattened row (float32 [N+1, V]).
+
+    Rows that were expanded already hold their logits.  The others (never
+    expanded) are scored by one extra draft pass over them: source = parent's
+    state, position = P_root + depth, K/V written to temporary cache rows past
+    the scratch area (on a copy of `kv`), visibility = committed prefix, the
+    ancestors' scratch rows and the row itself."""
+    cfg = W.cfg
+    N, K, D = cfg.N, cfg.K, cfg.D
+    p_root = int(tree["position"][0])
+    len_out = p_root + 1
+    root = info["root"]
+    out = np.zeros((N + 1, cfg.V), dtype=np.float32)
+    out[0] = root["logits"]
+    sel = sorted((n for n in info["nodes"] if n.get("selected")),
+                 key=lambda n: n["id"])
+    todo = []
+    for r, n in enumerate(sel, start=1):
+        if "logits" in n:
+            out[r] = n["logits"]
+        else:
+            todo.append((r, n))
+    if todo:
+        kv2 = kv.copy()
+        base = len_out + max(D - 1, 0) * K
+        src = np.stack([n["parent"]["a"] for _, n in todo])
+        vis = [np.concatenate([np.arange(len_out),
+                               len_out + np.asarray(n["parent"]["mask_slots"],
+                                                    dtype=np.int64),
+                               [base + i]]) for i, (_, n) in enumerate(todo)]
+        o = layer(W, kv2, src, [n["token"] for _, n in todo],
+                  pos=np.array([p_root + n["depth"] for _, n in todo]),
+                  dest=np.array([base + i for i in range(len(todo))]),
+                  visible=vis)
+        for i, (r, _) in enumerate(todo):
+            out[r] = o["logits"][i]
+    return out
+
+
+def decision_margin(cfg, tree_info) -> float:
+    """Smallest score gap at a selection boundary that decides the tree.
+
+    Boundaries: each per-layer expansion cut (K-th vs K+1-th value among the
+    layer's nodes), the final top-N cut, and the per-row top-K cut of a row
+    whose K-th child lies within 2e-3 of the lowest value selected by either
+    cut that sees it.  Inputs whose margin is below 1e-3 are redrawn."""
+    nodes = tree_info.get("nodes", [])
+    K, N, D = cfg.K, cfg.N, cfg.D
+    inf = float("inf")
+    margin = inf
+    if not nodes:
+        return margin
+    by_depth = {}
+    for n in nodes:
+        by_depth.setdefault(n["depth"], []).append(n)
+    cut_low = {}
+    for d, layer_nodes in by_depth.items():
+        sc = sorted((float(n["score"]) for n in layer_nodes), reverse=True)
+        if d < D and len(sc) > K:
+            margin = min(margin, sc[K - 1] - sc[K])
+        cut_low[d] = sc[min(K, len(sc)) - 1] if d < D else inf
+    allsc = sorted((float(n["score"]) for n in nodes), reverse=True)
+    fin_low = allsc[min(N, len(allsc)) - 1] if N > 0 else inf
+    if len(allsc) > N > 0:
+        margin = min(margin, allsc[N - 1] - allsc[N])
+    # per-row top-K cuts
+    parents = {}
+    for n in nodes:
+        parents.setdefault(id(n["parent"]), (n["parent"], []))[1].append(n)
+    for p, kids in parents.values():
+        lg = np.asarray(p["logits"], dtype=np.float64)
+        srt = np.sort(lg)[::-1]
+        if len(srt) <= K:
+            continue
+        gap = srt[K - 1] - srt[K]
+        kth = min(float(c["score"]) for c in kids)
+        d = kids[0]["depth"]
+        low = min(cut_low.get(d, inf), fin_low)
+        if kth + 2e-3 >= low:
+            margin = min(margin, gap)
+    return margin
+
+
+# ---------------------------------------------------------------------------
+# (4) verification
+# ---------------------------------------------------------------------------
+def verify_row(logits, child_tokens, T: float, u_child, u_bonus):
+    """One visited row of the verification walk.
+
+    Greedy (T == 0): x* = argmax (lowest id on ties); the child carrying x* is
+    accepted, else x* is the emitted token ([E1] 3.4, greedy tree drafting).
+
+    Sampling (T > 0): Algorithm 1 of [E1] ("Multi-round sampling for tree
+    structures") with target p = softmax(logits / T) and each child a point
+    mass proposal (the children are the deterministic top-k, so p_hat_i puts
+    all mass on t_i): child i is accepted when r_i < p(t_i) / 1; on rejection
+    p <- norm(max(0, p - onehot(t_i))), i.e. t_i's mass is removed and p is
+    renormalised; if every child is rejected one token is drawn from the
+    final p by inverse CDF over ascending ids using u_bonus.
+
+    `u_child(i)` / `u_bonus()` return the uniform for child i / the bonus.
+    Returns (accepted child index or None, emitted token or None, margin)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if T == 0:
+        x = int(np.argmax(lg))
+        for i, c in enumerate(child_tokens):
+            if c == x:
+                return i, None, float("inf")
+        return None, x, float("inf")
+    w = np.exp((lg - lg.max()) / T)
+    margin = float("inf")
+    for i, c in enumerate(child_tokens):
+        S = w.sum()
+        u = float(u_child(i))
+        thr = w[c] / S
+        margin = min(margin, abs(u - thr))
+        if u < thr:
+            return i, None, margin
+        w[c] = 0.0
+    S = w.sum()
+    ub = float(u_bonus())
+    if not S > 0.0:
+        # the children held all remaining mass: take the best other token
+        lg2 = lg.copy()
+        lg2[list(child_tokens)] = -np.inf
+        return None, int(np.argmax(lg2)), 0.0
+    cdf = np.cumsum(w) / S
+    tok = int(np.searchsorted(cdf, ub, side="right"))
+    tok = min(tok, len(w) - 1)
+    while w[tok] == 0.0 and tok > 0:   # never land on a zero-mass token
+        tok -= 1
+    lo = cdf[tok - 1] if tok > 0 else 0.0
+    margin = min(margin, abs(ub - cdf[tok]), abs(ub - lo) if tok > 0 else 1.0)
+    return None, tok, margin
+
+
+def verify(cfg, tree, target_logits, T: float, uniforms=None):
+    """Walk the flattened tree from the root ([E1] Algorithm 1, applied at
+    each visited row; [E1] "The Full Inference Loop": a >= 0 accepted draft
+    tokens plus one emitted token).
+
+    target_logits [N+1, V] float32: row r holds the target's next-token
+    logits after node r.  uniforms [N+1, K+1]: column i < K is the draw for
+    the i-th child of that row (ascending token id), column K the bonus.
+    Returns dict(accept_len, accepted_rows, tokens, bonus, margin)."""
+    D, K = cfg.D, cfg.K
+    v = 0
+    acc = []
+    margin = float("inf")
+    while True:
+        fc, nc = int(tree["first_child"][v]), int(tree["n_child"][v])
+        kids = list(range(fc, fc + nc)) if nc > 0 else []
+        ktok = [int(tree["token"][c]) for c in kids]
+        u = uniforms[v] if uniforms is not None else None
+        ci, tok, m = verify_row(target_logits[v], ktok, T,
+                                (lambda i: u[i]) if u is not None else None,
+                                (lambda: u[K]) if u is not None else None)
+        margin = min(margin, m)
+        if ci is not None:
+            v = kids[ci]
+            acc.append(v)
+            continue
+        bonus = tok
+        break
+    rows = np.full(D, -1, dtype=np.int32)
+    rows[: len(acc)] = acc
+    toks = np.full(D + 1, -1, dtype=np.int32)
+    for i, r in enumerate(acc):
+        toks[i] = tree["token"][r]
+    toks[len(acc)] = bonus
+    return {"accept_len": len(acc), "accepted_rows": rows, "tokens": toks,
+            "bonus": bonus, "margin": margin}
+
+
+# ---------------------------------------------------------------------------
+# commit of the accepted path ([M75] 0x05D)
+# ---------------------------------------------------------------------------
+def commit(cfg, tree, result, kv: DraftKV):
+    """Publish the accepted path into the draft KV and build the next seed.
+
+    [M75] 0x05D commits accepted state, discards unaccepted tree rows and
+    reseeds from the last verified target feature with the advanced token;
+    row maps come from the flatten metadata, never from token equality.
+
+    Draft row of node u (depth i) sits at position P_root + i and was computed
+    from (parent state, token of u).  Accepted nodes u_1..u_{a-1} each have a
+    child in the tree, so each was expanded and owns a scratch row; u_a owns
+    one only if it was expanded.  Kept rows move to cache index = position.
+    The next seed supplies the missing rows with real target features:
+      a == 0:                     [(row 0, bonus)]
+      u_a expanded:               [(row u_a, bonus)]
+      u_a not expanded:           [(row u_{a-1}, token u_a), (row u_a, bonus)]
+    where (row r, tok) means "fused target feature at flattened row r, joined
+    with token tok".  Returns (new_len, seed_rows, seed_tokens)."""
+    a = result["accept_len"]
+    rows = list(result["accepted_rows"][:a])
+    p_root = int(tree["position"][0])
+    len_out = p_root + 1
+    bonus = int(result["bonus"])
+    if a == 0:
+        keep, seed = [], [(0, bonus)]
+    elif tree["kv_slot"][rows[-1]] >= 0:
+        keep, seed = rows, [(rows[-1], bonus)]
+    else:
+        prev = rows[-2] if a >= 2 else 0
+        keep = rows[:-1]
+        seed = [(prev, int(tree["token"][rows[-1]])), (rows[-1], bonus)]
+    src = [len_out + int(tree["kv_slot"][r]) for r in keep]
+    dst = [p_root + int(tree["depth"][r]) for r in keep]
+    ksrc = kv.k[:, src].copy()
+    vsrc = kv.v[:, src].copy()
+    for i, dd in enumerate(dst):
+        kv.k[:, dd] = ksrc[:, i]
+        kv.v[:, dd] = vsrc[:, i]
+    new_len = len_out + len(keep)
+    return new_len, [s[0] for s in seed], [s[1] for s in seed]

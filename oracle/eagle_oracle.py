@@ -5,8 +5,11 @@ benchmark's CPU-baseline leg; nothing on the product path imports it.  It
 shares no code with the HIP library.
 
 Everything is NumPy float64.  A value that the method stores is rounded at the
-storage point: float64 -> float32 -> (bf16 when the drafter runs in bf16).
-Logits, log-sum-exp, log-probabilities and tree scores are float32 values.
+storage point.  Weights and the draft KV cache (and the rotated queries that
+meet it) use the drafter's storage type (bf16 or fp32); every activation
+(fused feature g, layer input x, attention output o, residual h, SwiGLU
+product t, draft state a, and the normalised GEMM inputs) is stored as
+float32.  Logits, log-sum-exp, log-probabilities and tree scores are float32.
 
 Sources (web pages; cited by title and section):
   [E3]  "EAGLE-3: Scaling up Inference Acceleration of Large Language Models
@@ -24,6 +27,7 @@ Sources (web pages; cited by title and section):
 
 Readings where the pages are silent (each also listed in the design notes):
   * fusion and input FCs carry no bias; LM head has no bias;
+  * precision: weights and draft KV in the storage type, activations float32;
   * the draft layer is a LLaMA pre-norm block: RMSNorm (eps 1e-5) -> attention
     with rotate-half RoPE -> residual -> RMSNorm -> SwiGLU -> residual; a final
     RMSNorm with its own gain precedes the LM head; the un-normed output `a`
@@ -138,10 +142,11 @@ def silu(x):
 # ---------------------------------------------------------------------------
 def fuse(W: Weights, low, mid, high) -> np.ndarray:
     """g = W_R [l; m; h] for each row ([E3] "Change 2: The fusion FC layer";
-    [M75] 0x08B): concat of the three k-dim taps, projected 3k -> k."""
+    [M75] 0x08B): concat of the three k-dim taps, projected 3k -> k.  The
+    taps arrive in the storage type; g is a float32 activation."""
     cat = np.concatenate([np.atleast_2d(low), np.atleast_2d(mid),
                           np.atleast_2d(high)], axis=-1).astype(np.float64)
-    return store(cat @ W.w_fuse.T, W.cfg.dtype)
+    return store(cat @ W.w_fuse.T, "fp32")
 
 
 # ---------------------------------------------------------------------------
@@ -193,14 +198,15 @@ def layer(W: Weights, kv: DraftKV, src, tok, pos, dest, visible):
     """
     cfg = W.cfg
     dt, eps = cfg.dtype, cfg.eps
+    f32 = "fp32"
     src = np.atleast_2d(np.asarray(src, dtype=np.float64))
     tok = np.asarray(tok, dtype=np.int64)
     R = src.shape[0]
     nq, nkv, hd = cfg.n_q, cfg.n_kv, cfg.hd
     group = nq // nkv
 
-    x = store(np.concatenate([src, W.embed[tok]], axis=1) @ W.w_in.T, dt)
-    n1 = rmsnorm(x, W.g_attn, eps, dt)
+    x = store(np.concatenate([src, W.embed[tok]], axis=1) @ W.w_in.T, f32)
+    n1 = rmsnorm(x, W.g_attn, eps, f32)
     q = rope((n1 @ W.wq.T).reshape(R, nq, hd), pos, cfg.theta)
     k = rope((n1 @ W.wk.T).reshape(R, nkv, hd), pos, cfg.theta)
     v = (n1 @ W.wv.T).reshape(R, nkv, hd)
@@ -214,12 +220,12 @@ def layer(W: Weights, kv: DraftKV, src, tok, pos, dest, visible):
         for hh in range(nq):
             g = hh // group
             o[r, hh] = attend(q[r, hh], kv.k[g, idx], kv.v[g, idx])
-    o = store(o, dt)
-    h = store(x + o.reshape(R, nq * hd) @ W.wo.T, dt)
-    n2 = rmsnorm(h, W.g_mlp, eps, dt)
-    t = store(silu(n2 @ W.w_gate.T) * (n2 @ W.w_up.T), dt)
-    a = store(h + t @ W.w_down.T, dt)
-    nf = rmsnorm(a, W.g_final, eps, dt)
+    o = store(o, f32)
+    h = store(x + o.reshape(R, nq * hd) @ W.wo.T, f32)
+    n2 = rmsnorm(h, W.g_mlp, eps, f32)
+    t = store(silu(n2 @ W.w_gate.T) * (n2 @ W.w_up.T), f32)
+    a = store(h + t @ W.w_down.T, f32)
+    nf = rmsnorm(a, W.g_final, eps, f32)
     logits = (nf @ W.w_lm.T).astype(np.float32)
     return {"x": x, "q": q, "k": k, "v": v, "o": o, "h": h, "t": t, "a": a,
             "logits": logits}

@@ -1,0 +1,217 @@
+"""EAGLE-3 draft-and-verify hot path on MI355X (gfx950).
+
+Thin PyTorch-facing binding over libeagle.so (include/eagle.h): every step of
+the path runs in the library's HIP kernels; this module only allocates tensors
+with torch and passes pointers.  Importing works without a GPU; calling needs
+the built library and a gfx950 device.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import EagleError, check, lib
+
+__all__ = ["DrafterShape", "Drafter", "KVCache", "EagleError", "lib",
+           "WEIGHT_NAMES"]
+
+WEIGHT_NAMES = ("w_fuse", "w_in", "embed", "wq", "wk", "wv", "wo", "w_gate",
+                "w_up", "w_down", "w_lm", "g_attn", "g_mlp", "g_final")
+
+
+@dataclass(frozen=True)
+class DrafterShape:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    dtype: str          # "bf16" | "fp32"
+    rope_theta: float
+    depth: int
+    topk: int
+    budget: int
+    max_batch: int
+    max_seed: int = 2
+    rms_eps: float = 1e-5
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c_config(self) -> _lib.Config:
+        return _lib.Config(self.hidden, self.n_q_heads, self.n_kv_heads,
+                           self.head_dim, self.ffn, self.vocab,
+                           0 if self.dtype == "bf16" else 1,
+                           float(self.rope_theta), float(self.rms_eps),
+                           self.depth, self.topk, self.budget, self.max_batch,
+                           self.max_seed)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class KVCache:
+    """Draft KV cache [B, n_kv, cap, hd] plus committed lengths [B] (int32)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, length: torch.Tensor):
+        assert k.shape == v.shape and k.dim() == 4 and k.is_contiguous()
+        self.k, self.v = k, v
+        self.length = length.to(torch.int32).contiguous()
+
+    @property
+    def cap(self) -> int:
+        return self.k.shape[2]
+
+    def c_kv(self, len_in, len_out) -> _lib.KV:
+        return _lib.KV(self.k.data_ptr(), self.v.data_ptr(), self.cap,
+                       None if len_in is None else len_in.data_ptr(),
+                       None if len_out is None else len_out.data_ptr())
+
+
+class Drafter:
+    """One drafter context: config, weights, workspace."""
+
+    def __init__(self, shape: DrafterShape, weights: dict, device="cuda"):
+        self.shape = shape
+        L = lib()
+        self._cfg = shape.c_config()
+        nbytes = L.eagle_workspace_bytes(ctypes.byref(self._cfg))
+        if nbytes == 0:
+            raise EagleError(2, "eagle_workspace_bytes (config rejected)")
+        self.weights = {}
+        for n in WEIGHT_NAMES:
+            t = weights[n]
+            if t.dtype != shape.torch_dtype or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"weight {n}: need contiguous {shape.torch_dtype} on GPU")
+            self.weights[n] = t
+        self._w = _lib.Weights(*[self.weights[n].data_ptr() for n in WEIGHT_NAMES])
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ctx = ctypes.c_void_p()
+        check(L.eagle_create(ctypes.byref(self._cfg), ctypes.byref(self._w),
+                             _ptr(self.workspace), nbytes, _stream(),
+                             ctypes.byref(ctx)), "eagle_create")
+        self._ctx = ctx
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            lib().eagle_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------
+    def device_status(self) -> int:
+        st = ctypes.c_int32(0)
+        check(lib().eagle_get_device_status(self._ctx, ctypes.byref(st),
+                                            _stream()), "eagle_get_device_status")
+        return int(st.value)
+
+    def fuse(self, low, mid, high, out=None):
+        rows = low.shape[0]
+        if out is None:
+            out = torch.empty(rows, self.shape.hidden, dtype=torch.float32,
+                              device=low.device)
+        check(lib().eagle_fuse_features(self._ctx, rows, _ptr(low), _ptr(mid),
+                                        _ptr(high), _ptr(out), _stream()),
+              "eagle_fuse_features")
+        return out
+
+    def draft_step(self, batch, rows_per_seq, src, token, position, dest,
+                   prefix_len, scratch_base, scratch_mask, kv: KVCache,
+                   a_out=None, topk_id=None, topk_logit=None, lse=None):
+        R = batch * rows_per_seq
+        dev = src.device
+        K = self.shape.topk
+        a_out = a_out if a_out is not None else torch.empty(
+            R, self.shape.hidden, dtype=torch.float32, device=dev)
+        topk_id = topk_id if topk_id is not None else torch.full(
+            (R, K), -1, dtype=torch.int32, device=dev)
+        topk_logit = topk_logit if topk_logit is not None else torch.full(
+            (R, K), float("nan"), dtype=torch.float32, device=dev)
+        lse = lse if lse is not None else torch.full(
+            (R,), float("nan"), dtype=torch.float32, device=dev)
+        ckv = kv.c_kv(None, None)
+        check(lib().eagle_draft_step(
+            self._ctx, batch, rows_per_seq, _ptr(src), _ptr(token),
+            _ptr(position), _ptr(dest), _ptr(prefix_len), _ptr(scratch_base),
+            _ptr(scratch_mask), ctypes.byref(ckv), _ptr(a_out), _ptr(topk_id),
+            _ptr(topk_logit), _ptr(lse), _stream()), "eagle_draft_step")
+        return a_out, topk_id, topk_logit, lse
+
+    def alloc_tree(self, batch, device="cuda"):
+        N1 = self.shape.budget + 1
+        W = (N1 + 63) // 64
+        i32 = dict(dtype=torch.int32, device=device)
+        t = {n: torch.empty(batch, N1, **i32) for n in (
+            "token", "parent", "depth", "position", "kv_slot", "first_child",
+            "n_child")}
+        t["score"] = torch.empty(batch, N1, dtype=torch.float32, device=device)
+        t["mask"] = torch.empty(batch, N1, W, dtype=torch.int64, device=device)
+        t["n_nodes"] = torch.empty(batch, **i32)
+        return t
+
+    @staticmethod
+    def _c_tree(t) -> _lib.Tree:
+        return _lib.Tree(*[t[n].data_ptr() for n in (
+            "token", "parent", "depth", "position", "kv_slot", "first_child",
+            "n_child", "score", "mask", "n_nodes")])
+
+    def draft_tree(self, seed_src, seed_token, seed_len, kv: KVCache,
+                   len_out=None, tree=None):
+        """seed_src [B, max_seed, H] float32; seed_token [B, max_seed];
+        seed_len [B].  Returns (tree dict, len_out [B])."""
+        B = seed_src.shape[0]
+        tree = tree if tree is not None else self.alloc_tree(B, seed_src.device)
+        len_out = len_out if len_out is not None else torch.empty(
+            B, dtype=torch.int32, device=seed_src.device)
+        ckv = kv.c_kv(kv.length, len_out)
+        ct = self._c_tree(tree)
+        check(lib().eagle_draft_tree(self._ctx, B, _ptr(seed_src),
+                                     _ptr(seed_token), _ptr(seed_len),
+                                     ctypes.byref(ckv), ctypes.byref(ct),
+                                     _stream()), "eagle_draft_tree")
+        return tree, len_out
+
+    def verify(self, tree, target_logits, temperature=0.0, uniforms=None,
+               kv: KVCache | None = None, kv_len_out=None, out=None):
+        B = tree["token"].shape[0]
+        D = self.shape.depth
+        dev = target_logits.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        if out is None:
+            out = {"accept_len": torch.empty(B, **i32),
+                   "accepted_rows": torch.empty(B, D, **i32),
+                   "tokens": torch.empty(B, D + 1, **i32),
+                   "seed_rows": torch.empty(B, 2, **i32),
+                   "seed_tokens": torch.empty(B, 2, **i32),
+                   "seed_len": torch.empty(B, **i32)}
+        ckv = None
+        if kv is not None:
+            if kv_len_out is None:
+                kv_len_out = torch.empty(B, **i32)
+            out["kv_len"] = kv_len_out
+            ckv = kv.c_kv(None, kv_len_out)
+        ct = self._c_tree(tree)
+        check(lib().eagle_verify_tree(
+            self._ctx, B, ctypes.byref(ct), _ptr(target_logits),
+            float(temperature), _ptr(uniforms),
+            ctypes.byref(ckv) if ckv is not None else None,
+            _ptr(out["accept_len"]), _ptr(out["accepted_rows"]),
+            _ptr(out["tokens"]), _ptr(out["seed_rows"]),
+            _ptr(out["seed_tokens"]), _ptr(out["seed_len"]), _stream()),
+            "eagle_verify_tree")
+        return out

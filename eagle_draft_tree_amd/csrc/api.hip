@@ -1,0 +1,564 @@
+// C ABI: argument validation, workspace layout and the launch sequence of a
+// draft pass, a tree and a verification.  No device memory is allocated here;
+// everything lives in the caller's workspace.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+
+#include "../../include/eagle.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace eagle;
+
+namespace {
+
+constexpr int kMaxSplit = 32;
+constexpr size_t kAlign = 256;
+
+struct Layout {
+  size_t total = 0;
+  size_t take(size_t bytes) {
+    const size_t o = total;
+    total += (bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  }
+};
+
+struct Offsets {
+  size_t x, h, a0, a1, q, o, t, rn1, rn2, rnf, ss, part, cnt, lm_val, lm_id,
+      lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
+      c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
+      len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
+      cnt_gemm, cnt_done, cnt_attn;
+  int R, Rpad, nmax_part, ncnt, ntile_lm, qg, ncand;
+  size_t total;
+};
+
+int esize(const eagle_config& c) { return c.dtype == EAGLE_BF16 ? 2 : 4; }
+
+eagle_status check_config(const eagle_config* c) {
+  if (c == nullptr) return EAGLE_EINVAL;
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->depth < 0 ||
+      c->topk < 1 || c->budget < 0 || c->max_batch < 1 || c->max_seed < 1 ||
+      !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
+    return EAGLE_EINVAL;
+  if (c->dtype != EAGLE_BF16 && c->dtype != EAGLE_FP32) return EAGLE_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return EAGLE_EUNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads) return EAGLE_EUNSUPPORTED;
+  if (c->hidden % 16 || c->ffn % 8 || c->vocab % 16) return EAGLE_EUNSUPPORTED;
+  if (c->topk > kMaxTopK || c->vocab < c->topk) return EAGLE_EUNSUPPORTED;
+  if (c->depth > 0 && (c->depth - 1) * c->topk > 64) return EAGLE_EUNSUPPORTED;
+  if (c->budget + 1 > 128 || c->max_seed > 4) return EAGLE_EUNSUPPORTED;
+  const int rps = std::max(c->max_seed, c->topk);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (rps * G > 128) return EAGLE_EUNSUPPORTED;
+  if (c->dtype == EAGLE_FP32 && (c->max_batch * rps > 64 || c->head_dim != 64))
+    return EAGLE_EUNSUPPORTED;
+  if (c->max_batch > 4096) return EAGLE_EUNSUPPORTED;
+  return EAGLE_OK;
+}
+
+Offsets make_layout(const eagle_config& c) {
+  Offsets f;
+  Layout L;
+  const int es = esize(c);
+  const int H = c.hidden, F = c.ffn, V = c.vocab, B = c.max_batch;
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  const int rps = std::max(c.max_seed, c.topk);
+  f.R = B * rps;
+  f.Rpad = (f.R + 63) / 64 * 64;
+  const size_t R = f.Rpad;
+  // activations are float; q is stored in the weight type like the KV cache
+  f.x = L.take(R * H * 4);
+  f.h = L.take(R * H * 4);
+  f.a0 = L.take(R * H * 4);
+  f.a1 = L.take(R * H * 4);
+  f.q = L.take(R * qd * es);
+  f.o = L.take(R * qd * 4);
+  f.t = L.take(R * F * 4);
+  f.rn1 = L.take(R * 4);
+  f.rn2 = L.take(R * 4);
+  f.rnf = L.take(R * 4);
+  f.ss = L.take(R * (H / 16) * 4);
+  f.nmax_part = std::max(H, qd + 2 * kd);
+  f.part = L.take(8 * R * f.nmax_part * 4);
+  f.ntile_lm = (V + 63) / 64;
+  f.lm_val = L.take(R * f.ntile_lm * c.topk * 4);
+  f.lm_id = L.take(R * f.ntile_lm * c.topk * 4);
+  f.lm_stat = L.take(R * f.ntile_lm * 2 * 4);
+  f.tk_id = L.take(R * c.topk * 4);
+  f.tk_val = L.take(R * c.topk * 4);
+  f.lse = L.take(R * 4);
+  f.qg = rps * (c.n_q_heads / c.n_kv_heads);
+  const size_t bk = static_cast<size_t>(B) * c.n_kv_heads * (kMaxSplit + 1) * f.qg;
+  f.at_o = L.take(bk * c.head_dim * 4);
+  f.at_ml = L.take(bk * 2 * 4);
+  for (int s = 0; s < 2; ++s)
+    for (int k = 0; k < 7; ++k) f.desc[s][k] = L.take(R * (k == 5 ? 8 : 4));
+  f.sbase = L.take(B * 4);
+  f.ncand = c.depth > 0 ? c.topk + (c.depth - 1) * c.topk * c.topk : 1;
+  const size_t BC = static_cast<size_t>(B) * f.ncand;
+  f.c_token = L.take(BC * 4);
+  f.c_parent = L.take(BC * 4);
+  f.c_slot = L.take(BC * 4);
+  f.c_row = L.take(BC * 4);
+  f.c_score = L.take(BC * 4);
+  f.c_mask = L.take(BC * 8);
+  f.c_depth = L.take(BC * 4);
+  f.n_cand = L.take(B * 4);
+  f.p_root = L.take(B * 4);
+  f.len_out = L.take(B * 4);
+  const size_t BN = static_cast<size_t>(B) * (c.budget + 1);
+  f.v_max = L.take(BN * 4);
+  f.v_sum = L.take(BN * 8);
+  f.v_arg = L.take(BN * 4);
+  f.v_bad = L.take(BN * 4);
+  // counters: zeroed once, every user resets what it touches
+  const int maxN = std::max(std::max(V, 2 * F), std::max(3 * H, qd + 2 * kd));
+  const size_t chunks = f.Rpad / 64;
+  f.counters_begin = L.total;
+  f.cnt_gemm = L.take(chunks * (maxN / 16 + 1) * 4);
+  f.cnt_done = L.take(chunks * 4);
+  f.cnt_attn = L.take(static_cast<size_t>(B) * c.n_kv_heads * 4);
+  f.status = L.take(4);
+  f.counters_end = L.total;
+  f.ncnt = static_cast<int>((f.counters_end - f.counters_begin) / 4);
+  f.total = L.total;
+  return f;
+}
+
+}  // namespace
+
+struct eagle_ctx {
+  eagle_config cfg;
+  eagle_weights w;
+  char* ws;
+  Offsets off;
+  int num_cus;
+  template <typename P> P* at(size_t o) const { return reinterpret_cast<P*>(ws + o); }
+  int* cnt() const { return at<int>(off.cnt_gemm); }
+  int* done() const { return at<int>(off.cnt_done); }
+  int* attn_cnt() const { return at<int>(off.cnt_attn); }
+  int* status() const { return at<int>(off.status); }
+};
+
+namespace {
+
+struct Rows {  // one pass's query rows
+  int batch, rps;
+  const void* src;           // rows gathered through src_row (or identity)
+  const int32_t* src_row;    // may be null: row r reads src row r
+  int src_rows;              // rows addressable in src
+  const int32_t *tok, *pos, *dest, *plen, *sbase;
+  const uint64_t* mask;
+  void* a_out;
+  int32_t* topk_id;
+  float* topk_val;
+  float* lse;
+};
+
+template <typename T>
+hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s) {
+  p.a_lo = 0;
+  if (sizeof(T) == 2)
+    for (int i = 0; i < p.nseg; ++i) p.a_lo |= p.seg[i].f32;
+  p.Mtot = c->off.Rpad;
+  p.part = c->at<float>(c->off.part);
+  p.part_cols = 8 * c->off.nmax_part;
+  p.cnt = c->cnt();
+  p.done = c->done();
+  p.eps = c->cfg.rms_eps;
+  plan_gemm(p, c->num_cus);
+  return launch_gemm<T>(p, s);
+}
+
+template <typename T>
+eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
+                       hipStream_t s) {
+  const eagle_config& cf = c->cfg;
+  const Offsets& f = c->off;
+  const int H = cf.hidden, F = cf.ffn, V = cf.vocab;
+  const int qd = cf.n_q_heads * cf.head_dim, kd = cf.n_kv_heads * cf.head_dim;
+  const int R = r.batch * r.rps;
+  hipError_t e;
+#define EAGLE_TRY(x)                 \
+  do {                               \
+    e = (x);                         \
+    if (e != hipSuccess) return EAGLE_EHIP; \
+  } while (0)
+
+  // a2 join: x = W_I [src ; E[tok]]
+  {
+    GemmParams p;
+    p.M = R; p.N = H; p.K = 2 * H; p.nseg = 2;
+    p.seg[0].base = r.src; p.seg[0].ld = H; p.seg[0].rowidx = r.src_row;
+    p.seg[0].rowlimit = r.src_rows; p.seg[0].width = H;
+    p.seg[1].base = c->w.embed; p.seg[1].ld = H; p.seg[1].rowidx = r.tok;
+    p.seg[1].rowlimit = V; p.seg[1].width = H; p.seg[1].f32 = 0;
+    p.w0 = c->w.w_in;
+    p.epi = EPI_STORE; p.out = c->at<char>(f.x); p.ldo = H;
+    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rn1);
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+  }
+  // a3 RMSNorm -> QKV -> RoPE -> q buffer + KV cache rows
+  {
+    GemmParams p;
+    p.M = R; p.N = qd + 2 * kd; p.K = H; p.nseg = 1;
+    p.seg[0].base = c->at<char>(f.x); p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].rnorm = c->at<float>(f.rn1); p.seg[0].gain = c->w.g_attn;
+    p.w0 = c->w.wq; p.w1 = c->w.wk; p.w2 = c->w.wv;
+    p.colmap = MAP_QKV; p.qkv_n0 = qd; p.qkv_n1 = kd; p.hd = cf.head_dim;
+    p.epi = EPI_QKV; p.out = c->at<char>(f.q); p.ldo = qd;
+    p.pos = r.pos; p.dest = r.dest; p.tok = r.tok; p.rows_per_seq = r.rps;
+    p.kc = kv->k; p.vc = kv->v; p.cap = kv->cap; p.nq = cf.n_q_heads;
+    p.nkv = cf.n_kv_heads; p.batch = r.batch; p.theta = cf.rope_theta;
+    p.status = c->status();
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+  }
+  // a4 tree attention
+  {
+    AttnParams p;
+    p.batch = r.batch; p.rows_per_seq = r.rps; p.nq = cf.n_q_heads;
+    p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.cap = kv->cap;
+    p.q = c->at<char>(f.q); p.o = c->at<float>(f.o);
+    p.kc = kv->k; p.vc = kv->v; p.tok = r.tok; p.plen = r.plen;
+    p.sbase = r.sbase; p.smask = r.mask;
+    int nsplit = std::min(kMaxSplit, std::max(1, (kv->cap + 63) / 64));
+    int chunk = (kv->cap + nsplit - 1) / nsplit;
+    chunk = std::max(64, (chunk + 63) / 64 * 64);
+    nsplit = std::max(1, (kv->cap + chunk - 1) / chunk);
+    p.nsplit = nsplit; p.chunk = chunk;
+    p.part_o = c->at<float>(f.at_o); p.part_ml = c->at<float>(f.at_ml);
+    p.cnt = c->attn_cnt();
+    p.scale = 1.0f / sqrtf(static_cast<float>(cf.head_dim));
+    EAGLE_TRY(launch_attention<T>(p, s));
+  }
+  // a5 h = x + Wo o
+  {
+    GemmParams p;
+    p.M = R; p.N = H; p.K = qd; p.nseg = 1;
+    p.seg[0].base = c->at<char>(f.o); p.seg[0].ld = qd; p.seg[0].width = qd;
+    p.w0 = c->w.wo;
+    p.epi = EPI_RESID; p.out = c->at<char>(f.h); p.ldo = H;
+    p.resid = c->at<float>(f.x); p.ldr = H;
+    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rn2);
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+  }
+  // a6 t = silu(Wg n2) * (Wu n2)
+  {
+    GemmParams p;
+    p.M = R; p.N = 2 * F; p.K = H; p.nseg = 1;
+    p.seg[0].base = c->at<char>(f.h); p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].rnorm = c->at<float>(f.rn2); p.seg[0].gain = c->w.g_mlp;
+    p.w0 = c->w.w_gate; p.w1 = c->w.w_up; p.colmap = MAP_SWIGLU;
+    p.epi = EPI_SWIGLU; p.out = c->at<char>(f.t); p.ldo = F;
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+  }
+  //    a = h + Wd t
+  {
+    GemmParams p;
+    p.M = R; p.N = H; p.K = F; p.nseg = 1;
+    p.seg[0].base = c->at<char>(f.t); p.seg[0].ld = F; p.seg[0].width = F;
+    p.w0 = c->w.w_down;
+    p.epi = EPI_RESID; p.out = r.a_out; p.ldo = H;
+    p.resid = c->at<float>(f.h); p.ldr = H;
+    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rnf);
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+  }
+  // a7 final norm -> LM head -> per-tile top-k -> merge
+  {
+    GemmParams p;
+    p.M = R; p.N = V; p.K = H; p.nseg = 1;
+    p.seg[0].base = r.a_out; p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].rnorm = c->at<float>(f.rnf); p.seg[0].gain = c->w.g_final;
+    p.w0 = c->w.w_lm;
+    p.epi = EPI_LMHEAD;
+    p.cand_val = c->at<float>(f.lm_val); p.cand_id = c->at<int32_t>(f.lm_id);
+    p.stat = c->at<float>(f.lm_stat); p.ntile_lm = f.ntile_lm; p.topk = cf.topk;
+    EAGLE_TRY(run_gemm<T>(c, p, s));
+    MergeParams m;
+    m.rows = R; m.ntile = f.ntile_lm; m.topk = cf.topk;
+    m.cand_val = p.cand_val; m.cand_id = p.cand_id; m.stat = p.stat;
+    m.tok = r.tok; m.out_id = r.topk_id; m.out_val = r.topk_val; m.out_lse = r.lse;
+    EAGLE_TRY(launch_merge(m, s));
+  }
+#undef EAGLE_TRY
+  return EAGLE_OK;
+}
+
+QueryDesc desc_of(eagle_ctx* c, int set) {
+  QueryDesc d;
+  const size_t* o = c->off.desc[set];
+  d.tok = c->at<int32_t>(o[0]);
+  d.src_row = c->at<int32_t>(o[1]);
+  d.pos = c->at<int32_t>(o[2]);
+  d.dest = c->at<int32_t>(o[3]);
+  d.plen = c->at<int32_t>(o[4]);
+  d.mask = c->at<uint64_t>(o[5]);
+  d.node = c->at<int32_t>(o[6]);
+  return d;
+}
+
+TreeState tree_state(eagle_ctx* c) {
+  TreeState t;
+  const Offsets& f = c->off;
+  t.c_token = c->at<int32_t>(f.c_token);
+  t.c_parent = c->at<int32_t>(f.c_parent);
+  t.c_slot = c->at<int32_t>(f.c_slot);
+  t.c_row = c->at<int32_t>(f.c_row);
+  t.c_score = c->at<float>(f.c_score);
+  t.c_mask = c->at<uint64_t>(f.c_mask);
+  t.c_depth = c->at<int32_t>(f.c_depth);
+  t.n_cand = c->at<int32_t>(f.n_cand);
+  t.p_root = c->at<int32_t>(f.p_root);
+  t.len_out = c->at<int32_t>(f.len_out);
+  t.ncand_max = f.ncand;
+  return t;
+}
+
+template <typename T>
+eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
+                             const int32_t* seed_token, const int32_t* seed_len,
+                             const eagle_kv* kv, const eagle_tree* out,
+                             hipStream_t s) {
+  const eagle_config& cf = c->cfg;
+  const Offsets& f = c->off;
+  const int K = cf.topk, D = cf.depth, N = cf.budget;
+  SeedParams sp;
+  sp.batch = batch; sp.s_max = cf.max_seed; sp.K = K; sp.D = D; sp.cap = kv->cap;
+  sp.seed_token = seed_token; sp.seed_len = seed_len; sp.len_in = kv->len_in;
+  sp.len_out = kv->len_out; sp.q = desc_of(c, 0);
+  sp.sbase = c->at<int32_t>(f.sbase); sp.ts = tree_state(c); sp.status = c->status();
+  if (launch_seed_setup(sp, s) != hipSuccess) return EAGLE_EHIP;
+
+  const int passes = (D == 0 || N == 0) ? 1 : D;
+  for (int d = 1; d <= passes; ++d) {
+    const int rps = d == 1 ? cf.max_seed : K;
+    QueryDesc cur = desc_of(c, (d - 1) & 1), nxt = desc_of(c, d & 1);
+    Rows r;
+    r.batch = batch; r.rps = rps;
+    if (d == 1) {
+      r.src = seed_src; r.src_row = cur.src_row; r.src_rows = batch * cf.max_seed;
+    } else {
+      r.src = c->at<char>((d - 1) % 2 ? f.a1 : f.a0);
+      r.src_row = cur.src_row; r.src_rows = f.Rpad;
+    }
+    r.tok = cur.tok; r.pos = cur.pos; r.dest = cur.dest; r.plen = cur.plen;
+    r.sbase = c->at<int32_t>(f.sbase); r.mask = cur.mask;
+    r.a_out = c->at<char>(d % 2 ? f.a1 : f.a0);
+    r.topk_id = c->at<int32_t>(f.tk_id); r.topk_val = c->at<float>(f.tk_val);
+    r.lse = c->at<float>(f.lse);
+    eagle_status st = run_layer<T>(c, r, kv, s);
+    if (st != EAGLE_OK) return st;
+    GrowParams g;
+    g.batch = batch; g.K = K; g.D = (D == 0 || N == 0) ? 0 : D; g.N = N;
+    g.pass = (D == 0 || N == 0) ? 1 : d;
+    g.rows_per_seq = rps; g.s_max = cf.max_seed;
+    g.topk_id = r.topk_id; g.topk_val = r.topk_val; g.lse = r.lse;
+    g.cur = cur; g.nxt = nxt; g.ts = tree_state(c);
+    g.seed_token = seed_token; g.seed_len = seed_len;
+    g.t_token = out->token; g.t_parent = out->parent; g.t_depth = out->depth;
+    g.t_pos = out->position; g.t_slot = out->kv_slot; g.t_first = out->first_child;
+    g.t_nchild = out->n_child; g.t_score = out->score; g.t_mask = out->mask;
+    g.t_n = out->n_nodes; g.mask_words = (N + 1 + 63) / 64;
+    if (launch_grow(g, s) != hipSuccess) return EAGLE_EHIP;
+  }
+  return EAGLE_OK;
+}
+
+bool null_tree(const eagle_tree* t) {
+  return t == nullptr || !t->token || !t->parent || !t->depth || !t->position ||
+         !t->kv_slot || !t->first_child || !t->n_child || !t->score || !t->mask ||
+         !t->n_nodes;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t eagle_workspace_bytes(const eagle_config* cfg) {
+  if (check_config(cfg) != EAGLE_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+eagle_status eagle_create(const eagle_config* cfg, const eagle_weights* w,
+                          void* workspace, size_t ws_bytes, hipStream_t stream,
+                          eagle_ctx** out) {
+  if (out == nullptr || w == nullptr || workspace == nullptr) return EAGLE_EINVAL;
+  *out = nullptr;
+  eagle_status st = check_config(cfg);
+  if (st != EAGLE_OK) return st;
+  const void* ptrs[] = {w->w_fuse, w->w_in, w->embed, w->wq, w->wk, w->wv, w->wo,
+                        w->w_gate, w->w_up, w->w_down, w->w_lm, w->g_attn,
+                        w->g_mlp, w->g_final};
+  for (const void* p : ptrs)
+    if (p == nullptr) return EAGLE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return EAGLE_EINVAL;
+  Offsets off = make_layout(*cfg);
+  if (ws_bytes < off.total) return EAGLE_EWORKSPACE;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess) return EAGLE_EHIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return EAGLE_EHIP;
+  eagle_ctx* c = new (std::nothrow) eagle_ctx;
+  if (c == nullptr) return EAGLE_EINVAL;
+  c->cfg = *cfg;
+  c->w = *w;
+  c->ws = static_cast<char*>(workspace);
+  c->off = off;
+  c->num_cus = cus;
+  const int64_t n = static_cast<int64_t>((off.counters_end - off.counters_begin) / 4);
+  if (launch_fill_i32(c->at<int32_t>(off.counters_begin), 0, n, stream) != hipSuccess) {
+    delete c;
+    return EAGLE_EHIP;
+  }
+  *out = c;
+  return EAGLE_OK;
+}
+
+void eagle_destroy(eagle_ctx* ctx) { delete ctx; }
+
+const char* eagle_status_str(eagle_status s) {
+  switch (s) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_EINVAL: return "invalid argument";
+    case EAGLE_EUNSUPPORTED: return "unsupported shape";
+    case EAGLE_EHIP: return "HIP launch or copy failed";
+    case EAGLE_ECAPACITY: return "draft KV cache capacity exceeded";
+    case EAGLE_ENONFINITE: return "non-finite target logits";
+    case EAGLE_EWORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+eagle_status eagle_get_device_status(eagle_ctx* ctx, int32_t* host_status,
+                                     hipStream_t stream) {
+  if (ctx == nullptr || host_status == nullptr) return EAGLE_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return EAGLE_EHIP;
+  if (hipMemcpy(host_status, ctx->status(), sizeof(int32_t), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return EAGLE_EHIP;
+  if (launch_fill_i32(ctx->status(), 0, 1, stream) != hipSuccess) return EAGLE_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return EAGLE_EHIP;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_fuse_features(eagle_ctx* ctx, int32_t rows, const void* low,
+                                 const void* mid, const void* high, void* g_out,
+                                 hipStream_t stream) {
+  if (ctx == nullptr) return EAGLE_EINVAL;
+  if (rows < 0 || rows > 65536) return EAGLE_EINVAL;
+  if (rows == 0) return EAGLE_OK;
+  if (!low || !mid || !high || !g_out) return EAGLE_EINVAL;
+  const int H = ctx->cfg.hidden;
+  const int es = esize(ctx->cfg);
+  const int step = ctx->off.Rpad;
+  for (int r0 = 0; r0 < rows; r0 += step) {
+    const int m = std::min(step, rows - r0);
+    GemmParams p;
+    p.M = m; p.N = H; p.K = 3 * H; p.nseg = 3;
+    const void* src[3] = {low, mid, high};
+    for (int i = 0; i < 3; ++i) {
+      p.seg[i].base = static_cast<const char*>(src[i]) + static_cast<size_t>(r0) * H * es;
+      p.seg[i].ld = H;
+      p.seg[i].width = H;
+      p.seg[i].f32 = 0;
+    }
+    p.w0 = ctx->w.w_fuse;
+    p.epi = EPI_STORE;
+    p.out = static_cast<float*>(g_out) + static_cast<size_t>(r0) * H;
+    p.ldo = H;
+    hipError_t e = ctx->cfg.dtype == EAGLE_BF16 ? run_gemm<uint16_t>(ctx, p, stream)
+                                                : run_gemm<float>(ctx, p, stream);
+    if (e != hipSuccess) return EAGLE_EHIP;
+  }
+  return EAGLE_OK;
+}
+
+eagle_status eagle_draft_step(eagle_ctx* ctx, int32_t batch, int32_t rows_per_seq,
+                              const void* src, const int32_t* token,
+                              const int32_t* position, const int32_t* dest,
+                              const int32_t* prefix_len, const int32_t* scratch_base,
+                              const uint64_t* scratch_mask, const eagle_kv* kv,
+                              void* a_out, int32_t* topk_id, float* topk_logit,
+                              float* lse, hipStream_t stream) {
+  if (ctx == nullptr || kv == nullptr) return EAGLE_EINVAL;
+  const eagle_config& cf = ctx->cfg;
+  if (batch < 1 || batch > cf.max_batch || rows_per_seq < 1 ||
+      rows_per_seq > std::max(cf.max_seed, cf.topk))
+    return EAGLE_EINVAL;
+  if (!src || !token || !position || !dest || !prefix_len || !scratch_base ||
+      !scratch_mask || !kv->k || !kv->v || kv->cap < 1 || !a_out || !topk_id ||
+      !topk_logit || !lse)
+    return EAGLE_EINVAL;
+  Rows r;
+  r.batch = batch; r.rps = rows_per_seq; r.src = src; r.src_row = nullptr;
+  r.src_rows = batch * rows_per_seq; r.tok = token; r.pos = position; r.dest = dest;
+  r.plen = prefix_len; r.sbase = scratch_base; r.mask = scratch_mask; r.a_out = a_out;
+  r.topk_id = topk_id; r.topk_val = topk_logit; r.lse = lse;
+  return cf.dtype == EAGLE_BF16 ? run_layer<uint16_t>(ctx, r, kv, stream)
+                                : run_layer<float>(ctx, r, kv, stream);
+}
+
+eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_src,
+                              const int32_t* seed_token, const int32_t* seed_len,
+                              const eagle_kv* kv, const eagle_tree* out,
+                              hipStream_t stream) {
+  if (ctx == nullptr || kv == nullptr || null_tree(out)) return EAGLE_EINVAL;
+  const eagle_config& cf = ctx->cfg;
+  if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
+  if (!seed_src || !seed_token || !seed_len || !kv->k || !kv->v || !kv->len_in ||
+      !kv->len_out || kv->cap < 1)
+    return EAGLE_EINVAL;
+  return cf.dtype == EAGLE_BF16
+             ? draft_tree_impl<uint16_t>(ctx, batch, seed_src, seed_token, seed_len, kv,
+                                         out, stream)
+             : draft_tree_impl<float>(ctx, batch, seed_src, seed_token, seed_len, kv, out,
+                                      stream);
+}
+
+eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                               const float* target_logits, float temperature,
+                               const float* uniforms, const eagle_kv* kv_or_null,
+                               int32_t* accept_len, int32_t* accepted_rows,
+                               int32_t* out_tokens, int32_t* next_seed_rows,
+                               int32_t* next_seed_tokens, int32_t* next_seed_len,
+                               hipStream_t stream) {
+  if (ctx == nullptr || null_tree(tree)) return EAGLE_EINVAL;
+  const eagle_config& cf = ctx->cfg;
+  if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return EAGLE_EINVAL;
+  if (!target_logits || !accept_len || !accepted_rows || !out_tokens ||
+      !next_seed_rows || !next_seed_tokens || !next_seed_len)
+    return EAGLE_EINVAL;
+  if (temperature > 0.f && uniforms == nullptr) return EAGLE_EINVAL;
+  if (kv_or_null && (!kv_or_null->k || !kv_or_null->v || !kv_or_null->len_out ||
+                     kv_or_null->cap < 1))
+    return EAGLE_EINVAL;
+  const Offsets& f = ctx->off;
+  VerifyParams p;
+  p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = cf.vocab;
+  p.T = temperature; p.logits = target_logits; p.uniforms = uniforms;
+  p.t_token = tree->token; p.t_parent = tree->parent; p.t_depth = tree->depth;
+  p.t_pos = tree->position; p.t_slot = tree->kv_slot; p.t_first = tree->first_child;
+  p.t_nchild = tree->n_child; p.t_n = tree->n_nodes;
+  p.row_max = ctx->at<float>(f.v_max); p.row_sum = ctx->at<double>(f.v_sum);
+  p.row_arg = ctx->at<int32_t>(f.v_arg); p.row_bad = ctx->at<int32_t>(f.v_bad);
+  p.accept_len = accept_len; p.accepted_rows = accepted_rows; p.out_tokens = out_tokens;
+  p.seed_rows = next_seed_rows; p.seed_tokens = next_seed_tokens;
+  p.seed_len = next_seed_len;
+  p.kc = kv_or_null ? kv_or_null->k : nullptr;
+  p.vc = kv_or_null ? kv_or_null->v : nullptr;
+  p.cap = kv_or_null ? kv_or_null->cap : 0;
+  p.kv_len = kv_or_null ? kv_or_null->len_out : nullptr;
+  p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.elem_bytes = esize(cf);
+  p.status = ctx->status();
+  return launch_verify(p, stream) == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Shared device helpers for the gfx950 kernels: element types, bf16
+// conversion, 8-element fragments and the 16x16x32 MFMA step, wave shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eagle {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 16;
+constexpr float kLogEps = -27.631021115928547f;  // log(1e-12) in float32
+
+// ----------------------------------------------------------------------------
+// bf16 <-> fp32
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+// round to nearest even; NaN kept quiet
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element traits.  T is the storage type: uint16_t (bf16 bits) or float.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return f2bf(v); }
+  // value after storage rounding
+  static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+
+// ----------------------------------------------------------------------------
+// 8-element fragments (one lane's share of a 16x16x32 MFMA operand)
+// ----------------------------------------------------------------------------
+template <typename T> struct Frag8;
+template <> struct Frag8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v = *reinterpret_cast<const u32x4*>(p);
+  }
+  __device__ __forceinline__ float get(int i) const {
+    uint32_t w = v[i >> 1];
+    return bf2f(static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  __device__ __forceinline__ void set_pair(int j, float lo, float hi) {
+    v[j] = static_cast<uint32_t>(f2bf(lo)) |
+           (static_cast<uint32_t>(f2bf(hi)) << 16);
+  }
+  __device__ __forceinline__ void set(int i, float x) {
+    uint32_t w = v[i >> 1];
+    uint32_t b = f2bf(x);
+    w = (i & 1) ? ((w & 0xffffu) | (b << 16)) : ((w & 0xffff0000u) | b);
+    v[i >> 1] = w;
+  }
+};
+template <> struct Frag8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void zero() {
+    a = f32x4{0.f, 0.f, 0.f, 0.f};
+    b = a;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+  __device__ __forceinline__ void set(int i, float x) {
+    if (i < 4) a[i] = x; else b[i - 4] = x;
+  }
+};
+
+// A operand of a weight-type MFMA built from float activations.  For bf16
+// weights the activation is carried as hi + lo bf16 parts (2^-17 relative),
+// so the product is accurate to float precision at twice the MFMA count.
+template <typename TW> struct AFrag;
+template <> struct AFrag<uint16_t> {
+  Frag8<uint16_t> hi, lo;
+  __device__ __forceinline__ void zero() { hi.zero(); lo.zero(); }
+  __device__ __forceinline__ void from_float(const Frag8<float>& x) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = x.get(2 * j), b = x.get(2 * j + 1);
+      hi.set_pair(j, a, b);
+      lo.set_pair(j, a - hi.get(2 * j), b - hi.get(2 * j + 1));
+    }
+  }
+  __device__ __forceinline__ void from_raw(const Frag8<uint16_t>& w) { hi = w; lo.zero(); }
+};
+template <> struct AFrag<float> {
+  Frag8<float> hi;
+  __device__ __forceinline__ void zero() { hi.zero(); }
+  __device__ __forceinline__ void from_float(const Frag8<float>& x) { hi = x; }
+  __device__ __forceinline__ void from_raw(const Frag8<float>& w) { hi = w; }
+};
+
+// acc[16x16] += A[16 x 32] * B[32 x 16] where lane l holds row/col (l % 16)
+// and the 8 k-values of lane group (l / 16).  Any k-permutation shared by A
+// and B gives the same sum, which the callers use to load wide contiguous
+// runs per lane.
+__device__ __forceinline__ f32x4 mfma16(const Frag8<uint16_t>& a,
+                                        const Frag8<uint16_t>& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
+      acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const Frag8<float>& a,
+                                        const Frag8<float>& b, f32x4 acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[i], b.a[i], acc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[i], b.b[i], acc, 0, 0, 0);
+  return acc;
+}
+
+// ----------------------------------------------------------------------------
+// wave helpers
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+__device__ __forceinline__ int shfl_xor(int v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+// (value, id) order used by every top-k: larger value first, then lower id
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Bitonic sort of one (value, id) pair per lane across the wave; afterwards
+// lane i holds the i-th best pair.
+__device__ __forceinline__ void wave_sort_desc(float& v, int& id) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      float ov = shfl_xor(v, j);
+      int oi = shfl_xor(id, j);
+      bool lower = (lane & j) == 0;           // lane is the lower of the pair
+      bool desc = (lane & k) == 0;            // this block sorts best-first
+      bool o_better = better(ov, oi, v, id);
+      bool take = desc ? (lower ? o_better : !o_better)
+                       : (lower ? !o_better : o_better);
+      if (ov == v && oi == id) take = false;
+      if (take) { v = ov; id = oi; }
+    }
+  }
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace eagle

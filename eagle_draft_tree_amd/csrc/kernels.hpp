@@ -1,0 +1,166 @@
+// Internal launch interfaces of the gfx950 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eagle {
+
+enum Epi : int {
+  EPI_STORE = 0,   // out = round(C)            (+ row sum of squares)
+  EPI_RESID = 1,   // out = round(C + resid)    (+ row sum of squares)
+  EPI_QKV = 2,     // RoPE on q/k, q -> buffer, k/v -> draft KV cache
+  EPI_SWIGLU = 3,  // out = round(silu(gate) * up)
+  EPI_LMHEAD = 4   // per-64-column top-k candidates + (max, sumexp)
+};
+enum ColMap : int { MAP_IDENT = 0, MAP_QKV = 1, MAP_SWIGLU = 2 };
+
+// One K-range segment of the A operand (rows of activations).
+struct ASeg {
+  const void* base = nullptr;     // [rows, ld] elements
+  int64_t ld = 0;
+  const int32_t* rowidx = nullptr;  // optional row gather; <0 or >= rowlimit -> zero row
+  int rowlimit = 0;
+  int width = 0;                  // K elements in this segment (multiple of 8)
+  const float* rnorm = nullptr;   // optional RMSNorm factor per A row
+  const void* gain = nullptr;     // RMSNorm gain [width] (weight type)
+  int f32 = 1;                    // elements are float activations (else weight type)
+};
+
+struct GemmParams {
+  int M = 0, N = 0, K = 0;        // N: logical output columns (multiple of 16)
+  int nseg = 1;
+  ASeg seg[3];
+  const void* w0 = nullptr;       // weights [rows, K]; see ColMap
+  const void* w1 = nullptr;
+  const void* w2 = nullptr;
+  int colmap = MAP_IDENT;
+  int qkv_n0 = 0, qkv_n1 = 0;     // columns served by w0, then w1, rest w2
+  int hd = 0;
+  int S = 1, WN = 1, WK = 4;      // split-K over WGs, waves along N and K
+  int a_lo = 0;                   // bf16 weights with float A rows: add the lo MFMA
+  int Mtot = 0;                   // padded rows of the partial buffer
+  float* part = nullptr;          // [S, Mtot, N] split-K partials
+  int part_cols = 0;              // S * N must not exceed this
+  int* cnt = nullptr;             // per (chunk, group) arrival counters
+  int* done = nullptr;            // per chunk finished-group counters
+  int epi = EPI_STORE;
+  void* out = nullptr;            // float activations (q: weight type)
+  int64_t ldo = 0;
+  const float* resid = nullptr;
+  int64_t ldr = 0;
+  float* ss = nullptr;            // [M, N/16] partial sums of squares
+  float* rnorm_out = nullptr;     // [M] 1/sqrt(mean(y^2) + eps)
+  float eps = 1e-5f;
+  // QKV epilogue
+  const int32_t* pos = nullptr;
+  const int32_t* dest = nullptr;
+  const int32_t* tok = nullptr;   // row valid iff tok[m] >= 0
+  int rows_per_seq = 1;
+  void* kc = nullptr;
+  void* vc = nullptr;
+  int cap = 0, nq = 0, nkv = 0, batch = 0;
+  float theta = 10000.f;
+  int* status = nullptr;
+  // LM-head epilogue
+  float* cand_val = nullptr;      // [M, ntile_lm, topk]
+  int32_t* cand_id = nullptr;
+  float* stat = nullptr;          // [M, ntile_lm, 2]
+  int ntile_lm = 0, topk = 0;
+};
+
+void plan_gemm(GemmParams& p, int num_cus);
+template <typename T> hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+// tree attention --------------------------------------------------------------
+struct AttnParams {
+  int batch = 0, rows_per_seq = 0;
+  int nq = 0, nkv = 0, hd = 0, cap = 0;
+  const void* q = nullptr;          // [rows, nq, hd]
+  float* o = nullptr;               // [rows, nq, hd] float
+  const void* kc = nullptr;         // [B, nkv, cap, hd]
+  const void* vc = nullptr;
+  const int32_t* tok = nullptr;     // row valid iff tok >= 0
+  const int32_t* plen = nullptr;    // [rows]
+  const int32_t* sbase = nullptr;   // [B]
+  const uint64_t* smask = nullptr;  // [rows]
+  int nsplit = 1, chunk = 64;
+  float* part_o = nullptr;          // [B, nkv, nsplit+1, QG, hd]
+  float* part_ml = nullptr;         // [B, nkv, nsplit+1, QG, 2]
+  int* cnt = nullptr;               // [B, nkv]
+  float scale = 1.f;
+};
+template <typename T> hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+// LM-head merge, tree growth, verification -----------------------------------
+struct MergeParams {
+  int rows = 0, ntile = 0, topk = 0;
+  const float* cand_val = nullptr;
+  const int32_t* cand_id = nullptr;
+  const float* stat = nullptr;
+  const int32_t* tok = nullptr;      // only rows with tok >= 0 are merged
+  int32_t* out_id = nullptr;         // [rows, topk]
+  float* out_val = nullptr;          // [rows, topk]
+  float* out_lse = nullptr;          // [rows]
+};
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
+struct TreeState {
+  // candidates [B, ncand_max]
+  int32_t* c_token; int32_t* c_parent; int32_t* c_slot; int32_t* c_row;
+  float* c_score; uint64_t* c_mask; int32_t* c_depth;
+  int32_t* n_cand;        // [B]
+  int32_t* p_root;        // [B] root position
+  int32_t* len_out;       // [B]
+  int ncand_max;
+};
+
+struct QueryDesc {  // one pass's query rows, [B * rows_per_seq] each
+  int32_t* tok; int32_t* src_row; int32_t* pos; int32_t* dest; int32_t* plen;
+  uint64_t* mask; int32_t* node;
+};
+
+struct SeedParams {
+  int batch, s_max, K, D, cap;
+  const int32_t* seed_token; const int32_t* seed_len; const int32_t* len_in;
+  int32_t* len_out;
+  QueryDesc q;        // pass-1 rows [B * s_max]
+  int32_t* sbase;     // [B] scratch base = len_out
+  TreeState ts;
+  int* status;
+};
+hipError_t launch_seed_setup(const SeedParams& p, hipStream_t s);
+
+struct GrowParams {
+  int batch, K, D, N, pass, rows_per_seq, s_max;
+  const int32_t* topk_id; const float* topk_val; const float* lse;
+  QueryDesc cur;      // this pass's rows
+  QueryDesc nxt;      // next pass's rows [B * K]
+  TreeState ts;
+  const int32_t* seed_token; const int32_t* seed_len;
+  // final outputs
+  int32_t *t_token, *t_parent, *t_depth, *t_pos, *t_slot, *t_first, *t_nchild;
+  float* t_score; uint64_t* t_mask; int32_t* t_n;
+  int mask_words;
+};
+hipError_t launch_grow(const GrowParams& p, hipStream_t s);
+
+struct VerifyParams {
+  int batch, N, K, D, V;
+  float T;
+  const float* logits;      // [B, N+1, V]
+  const float* uniforms;    // [B, N+1, K+1] or null
+  const int32_t *t_token, *t_parent, *t_depth, *t_pos, *t_slot, *t_first,
+      *t_nchild, *t_n;
+  float* row_max; double* row_sum; int32_t* row_arg; int32_t* row_bad;
+  int32_t *accept_len, *accepted_rows, *out_tokens, *seed_rows, *seed_tokens,
+      *seed_len;
+  void* kc; void* vc; int cap, nkv, hd; int32_t* kv_len;  // kc null: no commit
+  int elem_bytes;
+  int* status;
+};
+hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+}  // namespace eagle

@@ -1,0 +1,666 @@
+// LM-head top-k merge, EAGLE-2 tree growth / rerank / flatten, and tree
+// verification with the accepted-path commit.  These kernels move little
+// data; they are latency kernels built from wave shuffles and LDS counting.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace eagle {
+
+constexpr int kMaxCand = 16 + 7 * 256;  // >= K + (D-1) K^2 when (D-1)K <= 64
+constexpr int kMaxPath = 72;            // >= D + 1 when (D-1)K <= 64
+
+// ============================================================================
+// merge: per row, top-k over the LM-head tiles' candidates + log-sum-exp
+// ============================================================================
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  __shared__ float sv[4 * kMaxTopK];
+  __shared__ int si[4 * kMaxTopK];
+  __shared__ float sm[256], ss[256];
+  const int row = blockIdx.x;
+  if (p.tok[row] < 0) return;
+  const int K = p.topk;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int64_t base = static_cast<int64_t>(row) * p.ntile;
+
+  // thread-local sorted top-K
+  float lv[kMaxTopK];
+  int li[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+  const int ncand = p.ntile * K;
+  for (int idx = threadIdx.x; idx < ncand; idx += 256) {
+    const float v = p.cand_val[base * K + idx];
+    const int id = p.cand_id[base * K + idx];
+    if (!better(v, id, lv[K - 1], li[K - 1])) continue;
+#pragma unroll
+    for (int j = kMaxTopK - 1; j >= 0; --j) {
+      if (j >= K) continue;
+      if (better(v, id, lv[j], li[j])) {
+        if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
+          lv[j] = lv[j - 1];
+          li[j] = li[j - 1];
+        } else {
+          lv[j] = v;
+          li[j] = id;
+        }
+      }
+    }
+  }
+  // wave merge: K rounds of "pop the best head"
+  for (int r = 0; r < K; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = shfl_xor(bv, m);
+      const int oi = shfl_xor(bi, m);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lv[0] == bv && li[0] == bi) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK - 1; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+      lv[kMaxTopK - 1] = -INFINITY;
+      li[kMaxTopK - 1] = 0x7fffffff;
+    }
+    if (lane == 0) { sv[wave * K + r] = bv; si[wave * K + r] = bi; }
+  }
+  // log-sum-exp over tile statistics
+  float M = -INFINITY, S = 0.f;
+  for (int t = threadIdx.x; t < p.ntile; t += 256) {
+    const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
+    if (mx == -INFINITY) continue;
+    const float nm = fmaxf(M, mx);
+    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
+    M = nm;
+  }
+  sm[threadIdx.x] = M;
+  ss[threadIdx.x] = S;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      const float m1 = sm[threadIdx.x], m2 = sm[threadIdx.x + w];
+      const float s1 = ss[threadIdx.x], s2 = ss[threadIdx.x + w];
+      const float nm = fmaxf(m1, m2);
+      float s = 0.f;
+      if (nm != -INFINITY)
+        s = (m1 == -INFINITY ? 0.f : s1 * expf(m1 - nm)) +
+            (m2 == -INFINITY ? 0.f : s2 * expf(m2 - nm));
+      sm[threadIdx.x] = nm;
+      ss[threadIdx.x] = s;
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    float v = lane < 4 * K ? sv[lane] : -INFINITY;
+    int id = lane < 4 * K ? si[lane] : 0x7fffffff;
+    wave_sort_desc(v, id);
+    if (lane < K) {
+      p.out_id[static_cast<int64_t>(row) * K + lane] = id;
+      p.out_val[static_cast<int64_t>(row) * K + lane] = v;
+    }
+    if (lane == 0) p.out_lse[row] = sm[0] + logf(ss[0]);
+  }
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(p.rows), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// pass-1 query rows from the seed rows
+// ============================================================================
+__global__ void seed_setup_kernel(SeedParams p) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= p.batch) return;
+  const int len_in = p.len_in[b];
+  const int sl = p.seed_len[b];
+  const int scratch = p.D > 0 ? (p.D - 1) * p.K : 0;
+  bool ok = sl >= 1 && sl <= p.s_max && len_in >= 0 &&
+            static_cast<int64_t>(len_in) + sl + scratch <= p.cap;
+  if (!ok && p.status != nullptr) atomicOr(p.status, 1 << 4);
+  const int len_out = ok ? len_in + sl : max(len_in, 0);
+  p.len_out[b] = len_out;
+  p.ts.len_out[b] = len_out;
+  p.ts.p_root[b] = ok ? len_out - 1 : -1;
+  p.ts.n_cand[b] = 0;
+  p.sbase[b] = len_out;
+  for (int i = 0; i < p.s_max; ++i) {
+    const int r = b * p.s_max + i;
+    const int tok = (ok && i < sl) ? p.seed_token[r] : -1;
+    p.q.tok[r] = tok;
+    p.q.src_row[r] = r;
+    p.q.pos[r] = len_in + i;
+    p.q.dest[r] = len_in + i;
+    p.q.plen[r] = len_in + i + 1;
+    p.q.mask[r] = 0ull;
+    p.q.node[r] = -1;
+  }
+}
+
+hipError_t launch_seed_setup(const SeedParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(seed_setup_kernel, dim3((p.batch + 63) / 64), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// tree growth after one draft pass; final rerank + flatten after the last
+// ============================================================================
+__device__ __forceinline__ bool cand_better(float sa, int ia, float sb, int ib) {
+  // (-value, depth, node id): node ids grow with depth, so id breaks both ties
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
+  __shared__ float s_score[kMaxCand];
+  __shared__ int s_flag[kMaxCand];
+  __shared__ int s_scan[256];
+  __shared__ int s_prow[128], s_first[128], s_nch[128];
+  const int b = blockIdx.x;
+  const int K = p.K, D = p.D, N = p.N;
+  const int tid = threadIdx.x;
+  const TreeState& ts = p.ts;
+  const int64_t cb = static_cast<int64_t>(b) * ts.ncand_max;
+  const int p_root = ts.p_root[b];
+  const int len_out = ts.len_out[b];
+  const bool last = p.pass >= D;
+  const int rows1 = p.N + 1;
+  const int W = p.mask_words;
+
+  auto write_root_only = [&](bool valid) {
+    for (int r = tid; r < rows1; r += 256) {
+      const int64_t o = static_cast<int64_t>(b) * rows1 + r;
+      const bool root = r == 0 && valid;
+      p.t_token[o] = root ? p.seed_token[b * p.s_max + p.seed_len[b] - 1] : -1;
+      p.t_parent[o] = -1;
+      p.t_depth[o] = root ? 0 : -1;
+      p.t_pos[o] = root ? p_root : -1;
+      p.t_slot[o] = -1;
+      p.t_first[o] = -1;
+      p.t_nchild[o] = 0;
+      p.t_score[o] = 0.f;
+      for (int w = 0; w < W; ++w) p.t_mask[o * W + w] = (root && w == 0) ? 1ull : 0ull;
+    }
+    if (tid == 0) p.t_n[b] = valid ? 0 : -1;
+  };
+
+  if (p_root < 0) {  // sequence rejected at seed time
+    if (!last) {
+      for (int r = tid; r < K; r += 256) p.nxt.tok[b * K + r] = -1;
+    } else {
+      write_root_only(false);
+    }
+    return;
+  }
+  if (N == 0 || D == 0) {
+    write_root_only(true);
+    return;
+  }
+
+  // ---- create this pass's children ----
+  const int first = ts.n_cand[b];
+  const int nrows = p.pass == 1 ? 1 : K;
+  const int nnew = nrows * K;
+  if (tid < nnew) {
+    const int rr = tid / K, cc = tid % K;
+    const int row = p.pass == 1 ? b * p.s_max + p.seed_len[b] - 1 : b * K + rr;
+    const int* ids = p.topk_id + static_cast<int64_t>(row) * K;
+    const int my = ids[cc];
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += ids[j] < my;
+    const int node = first + rr * K + rank;
+    const int parent = p.pass == 1 ? -1 : p.cur.node[row];
+    const float ps = parent < 0 ? 0.f : ts.c_score[cb + parent];
+    float lp = p.topk_val[static_cast<int64_t>(row) * K + cc] - p.lse[row];
+    lp = fmaxf(lp, kLogEps);
+    ts.c_token[cb + node] = my;
+    ts.c_parent[cb + node] = parent;
+    ts.c_depth[cb + node] = p.pass;
+    ts.c_score[cb + node] = ps + lp;
+    ts.c_slot[cb + node] = -1;
+    ts.c_row[cb + node] = row;
+    ts.c_mask[cb + node] = parent < 0 ? 0ull : ts.c_mask[cb + parent];
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int ncand = first + nnew;
+  if (tid == 0) ts.n_cand[b] = ncand;
+
+  if (!last) {
+    // ---- expand the K best of the new layer ----
+    for (int i = tid; i < nnew; i += 256) s_score[i] = ts.c_score[cb + first + i];
+    __syncthreads();
+    for (int i = tid; i < nnew; i += 256) {
+      int rank = 0;
+      const float si = s_score[i];
+      for (int j = 0; j < nnew; ++j) rank += cand_better(s_score[j], j, si, i);
+      s_flag[i] = rank < K;
+    }
+    __syncthreads();
+    for (int i = tid; i < nnew; i += 256) {
+      if (!s_flag[i]) continue;
+      int r = 0;
+      for (int j = 0; j < i; ++j) r += s_flag[j];
+      const int node = first + i;
+      const int slot = (p.pass - 1) * K + r;
+      const uint64_t m = ts.c_mask[cb + node] | (1ull << slot);
+      ts.c_slot[cb + node] = slot;
+      ts.c_mask[cb + node] = m;
+      const int q = b * K + r;
+      p.nxt.tok[q] = ts.c_token[cb + node];
+      p.nxt.src_row[q] = ts.c_row[cb + node];
+      p.nxt.pos[q] = p_root + p.pass;
+      p.nxt.dest[q] = len_out + slot;
+      p.nxt.plen[q] = len_out;
+      p.nxt.mask[q] = m;
+      p.nxt.node[q] = node;
+    }
+    return;
+  }
+
+  // ---- final: top-N of all candidates, flatten ----
+  for (int i = tid; i < ncand; i += 256) s_score[i] = ts.c_score[cb + i];
+  __syncthreads();
+  for (int i = tid; i < ncand; i += 256) {
+    int rank = 0;
+    const float si = s_score[i];
+    for (int j = 0; j < ncand; ++j) rank += cand_better(s_score[j], j, si, i);
+    s_flag[i] = rank < N;
+  }
+  __syncthreads();
+  // exclusive scan of the flags over contiguous chunks
+  const int per = (ncand + 255) / 256;
+  const int lo = tid * per, hi = min(ncand, lo + per);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) cnt += s_flag[i];
+  s_scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int run = s_scan[tid] - cnt;
+  for (int i = lo; i < hi; ++i) {
+    if (s_flag[i]) {
+      s_flag[i] = 1 + run;  // row of node i
+      ++run;
+    } else {
+      s_flag[i] = 0;
+    }
+  }
+  const int nsel = s_scan[255];
+  for (int r = tid; r < 128; r += 256) { s_prow[r] = -1; s_first[r] = 0x7fffffff; s_nch[r] = 0; }
+  __syncthreads();
+  const int64_t ob = static_cast<int64_t>(b) * rows1;
+  for (int i = tid; i < ncand; i += 256) {
+    const int r = s_flag[i];
+    if (r == 0) continue;
+    const int par = ts.c_parent[cb + i];
+    const int prow = par < 0 ? 0 : s_flag[par];
+    const int dep = ts.c_depth[cb + i];
+    s_prow[r] = prow;
+    atomicMin(&s_first[prow], r);
+    atomicAdd(&s_nch[prow], 1);
+    p.t_token[ob + r] = ts.c_token[cb + i];
+    p.t_parent[ob + r] = prow;
+    p.t_depth[ob + r] = dep;
+    p.t_pos[ob + r] = p_root + dep;
+    p.t_slot[ob + r] = ts.c_slot[cb + i];
+    p.t_score[ob + r] = s_score[i];
+  }
+  __syncthreads();
+  for (int r = tid; r < rows1; r += 256) {
+    const int64_t o = ob + r;
+    if (r == 0) {
+      p.t_token[o] = p.seed_token[b * p.s_max + p.seed_len[b] - 1];
+      p.t_parent[o] = -1;
+      p.t_depth[o] = 0;
+      p.t_pos[o] = p_root;
+      p.t_slot[o] = -1;
+      p.t_score[o] = 0.f;
+    } else if (r > nsel) {
+      p.t_token[o] = -1;
+      p.t_parent[o] = -1;
+      p.t_depth[o] = -1;
+      p.t_pos[o] = -1;
+      p.t_slot[o] = -1;
+      p.t_score[o] = 0.f;
+    }
+    const bool live = r <= nsel;
+    p.t_first[o] = (live && s_nch[r] > 0) ? s_first[r] : -1;
+    p.t_nchild[o] = live ? s_nch[r] : 0;
+    uint64_t bits[2] = {0ull, 0ull};
+    if (live) {
+      int a = r;
+      while (a >= 0) {
+        bits[a >> 6] |= 1ull << (a & 63);
+        a = a == 0 ? -1 : s_prow[a];
+      }
+    }
+    for (int w = 0; w < W; ++w) p.t_mask[o * W + w] = bits[w];
+  }
+  if (tid == 0) p.t_n[b] = nsel;
+}
+
+hipError_t launch_grow(const GrowParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(grow_kernel, dim3(p.batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// verification
+// ============================================================================
+__device__ __forceinline__ float wexp(float l, float m, float T) {
+  return expf((l - m) / T);
+}
+
+__global__ __launch_bounds__(256) void row_stats_kernel(VerifyParams p) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ double sd[256];
+  __shared__ int sbad;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int n = p.t_n[b];
+  if (n < 0 || r > n) return;
+  const int rows1 = p.N + 1;
+  const int64_t o = static_cast<int64_t>(b) * rows1 + r;
+  const float* lg = p.logits + o * p.V;
+  const int tid = threadIdx.x;
+  if (tid == 0) sbad = 0;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  bool bad = false;
+  for (int i = tid; i < p.V; i += 256) {
+    const float v = lg[i];
+    if (!isfinite(v)) bad = true;
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  sv[tid] = bv;
+  si[tid] = bi;
+  __syncthreads();
+  if (bad) atomicOr(&sbad, 1);
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w && better(sv[tid + w], si[tid + w], sv[tid], si[tid])) {
+      sv[tid] = sv[tid + w];
+      si[tid] = si[tid + w];
+    }
+    __syncthreads();
+  }
+  const float mx = sv[0];
+  if (p.T > 0.f) {
+    double acc = 0.0;
+    for (int i = tid; i < p.V; i += 256) acc += static_cast<double>(wexp(lg[i], mx, p.T));
+    sd[tid] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (tid < w) sd[tid] += sd[tid + w];
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    p.row_max[o] = mx;
+    p.row_arg[o] = si[0];
+    p.row_sum[o] = p.T > 0.f ? sd[0] : 0.0;
+    p.row_bad[o] = sbad;
+  }
+}
+
+__global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
+  __shared__ int s_kids[kMaxTopK];
+  __shared__ int s_nk, s_row, s_need_res, s_bad, s_a, s_bonus;
+  __shared__ int s_acc[kMaxPath];
+  __shared__ double s_part[256];
+  __shared__ int s_pick[256];
+  __shared__ int s_kept[kMaxPath];
+  __shared__ int s_nkept;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rows1 = p.N + 1;
+  const int64_t ob = static_cast<int64_t>(b) * rows1;
+  const int n = p.t_n[b];
+  if (n < 0) {
+    if (tid == 0) {
+      p.accept_len[b] = -1;
+      for (int i = 0; i < p.D; ++i) p.accepted_rows[b * p.D + i] = -1;
+      for (int i = 0; i <= p.D; ++i) p.out_tokens[b * (p.D + 1) + i] = -1;
+      p.seed_len[b] = 0;
+      p.seed_rows[2 * b] = p.seed_rows[2 * b + 1] = -1;
+      p.seed_tokens[2 * b] = p.seed_tokens[2 * b + 1] = -1;
+    }
+    return;
+  }
+
+  if (tid == 0) {
+    int v = 0, a = 0, bad = 0, need = 0, bonus = -1;
+    while (true) {
+      if (p.row_bad[ob + v]) { bad = 1; break; }
+      const int fc = p.t_first[ob + v], nc = p.t_nchild[ob + v];
+      if (nc < 0 || nc > kMaxTopK || (nc > 0 && (fc < 1 || fc + nc > rows1))) {
+        bad = 1;
+        break;
+      }
+      const float* lg = p.logits + (ob + v) * p.V;
+      int nxt = -1;
+      if (p.T == 0.f) {
+        const int x = p.row_arg[ob + v];
+        for (int j = 0; j < nc; ++j)
+          if (p.t_token[ob + fc + j] == x) nxt = fc + j;
+        if (nxt < 0) { bonus = x; break; }
+      } else {
+        double S = p.row_sum[ob + v];
+        const float mx = p.row_max[ob + v];
+        const float* u = p.uniforms + (ob + v) * (p.K + 1);
+        for (int j = 0; j < nc; ++j) {
+          const int tok = p.t_token[ob + fc + j];
+          s_kids[j] = tok;
+          const double w = static_cast<double>(wexp(lg[tok], mx, p.T));
+          if (static_cast<double>(u[j]) * S < w) { nxt = fc + j; break; }
+          S -= w;
+        }
+        if (nxt < 0) {
+          need = 1;
+          s_nk = nc;
+          break;
+        }
+      }
+      if (a >= p.D || a >= kMaxPath) { bad = 1; break; }  // malformed tree
+      s_acc[a++] = nxt;
+      v = nxt;
+    }
+    s_row = v;
+    s_need_res = need;
+    s_bad = bad;
+    s_a = a;
+    s_bonus = bonus;
+  }
+  __syncthreads();
+
+  if (s_need_res && !s_bad) {
+    // residual draw at row v: children's tokens removed, inverse CDF
+    const int v = s_row;
+    const float* lg = p.logits + (ob + v) * p.V;
+    const float mx = p.row_max[ob + v];
+    const int nk = s_nk;
+    const int per = (p.V + 255) / 256;
+    const int lo = tid * per, hi = min(p.V, lo + per);
+    double part = 0.0;
+    for (int i = lo; i < hi; ++i) {
+      bool kid = false;
+      for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+      if (!kid) part += static_cast<double>(wexp(lg[i], mx, p.T));
+    }
+    s_part[tid] = part;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const double t = tid >= off ? s_part[tid - off] : 0.0;
+      __syncthreads();
+      s_part[tid] += t;
+      __syncthreads();
+    }
+    const double total = s_part[255];
+    const double excl = s_part[tid] - part;
+    const double u = static_cast<double>(p.uniforms[(ob + v) * (p.K + 1) + p.K]);
+    const double thr = u * total;
+    int pick = -1;
+    if (total > 0.0) {
+      if (thr >= excl && thr < excl + part) {
+        double cum = excl;
+        for (int i = lo; i < hi && pick < 0; ++i) {
+          bool kid = false;
+          for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+          if (kid) continue;
+          cum += static_cast<double>(wexp(lg[i], mx, p.T));
+          if (cum > thr) pick = i;
+        }
+      }
+      s_pick[tid] = pick;
+      __syncthreads();
+      if (tid == 0) {
+        int best = -1;
+        for (int t = 0; t < 256 && best < 0; ++t) best = s_pick[t];
+        s_bonus = best;
+      }
+      __syncthreads();
+      if (s_bonus < 0) {  // rounding put the threshold past the last mass
+        int lastnz = -1;
+        for (int i = lo; i < hi; ++i) {
+          bool kid = false;
+          for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+          if (!kid && wexp(lg[i], mx, p.T) > 0.f) lastnz = i;
+        }
+        s_pick[tid] = lastnz;
+        __syncthreads();
+        if (tid == 0) {
+          int best = -1;
+          for (int t = 0; t < 256; ++t) best = max(best, s_pick[t]);
+          s_bonus = best;
+        }
+      }
+    } else {
+      // the children held all the mass: best remaining token
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = lo; i < hi; ++i) {
+        bool kid = false;
+        for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+        if (!kid && better(lg[i], i, bv, bi)) { bv = lg[i]; bi = i; }
+      }
+      s_part[tid] = bv;
+      s_pick[tid] = bi;
+      __syncthreads();
+      if (tid == 0) {
+        float best = -INFINITY;
+        int bid = 0x7fffffff;
+        for (int t = 0; t < 256; ++t)
+          if (better(static_cast<float>(s_part[t]), s_pick[t], best, bid)) {
+            best = static_cast<float>(s_part[t]);
+            bid = s_pick[t];
+          }
+        s_bonus = bid;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs, next seed, commit ----
+  const int a = s_a;
+  const bool bad = s_bad;
+  const int p_root = p.t_pos[ob];
+  const int len_out = p_root + 1;
+  if (tid == 0) {
+    if (bad) {
+      atomicOr(p.status, 1 << 5);
+      p.accept_len[b] = -1;
+      for (int i = 0; i < p.D; ++i) p.accepted_rows[b * p.D + i] = -1;
+      for (int i = 0; i <= p.D; ++i) p.out_tokens[b * (p.D + 1) + i] = -1;
+      p.seed_len[b] = 0;
+      p.seed_rows[2 * b] = p.seed_rows[2 * b + 1] = -1;
+      p.seed_tokens[2 * b] = p.seed_tokens[2 * b + 1] = -1;
+      s_nkept = 0;
+    } else {
+      const int bonus = s_bonus;
+      p.accept_len[b] = a;
+      for (int i = 0; i < p.D; ++i) p.accepted_rows[b * p.D + i] = i < a ? s_acc[i] : -1;
+      for (int i = 0; i <= p.D; ++i) {
+        int t = -1;
+        if (i < a) t = p.t_token[ob + s_acc[i]];
+        else if (i == a) t = bonus;
+        p.out_tokens[b * (p.D + 1) + i] = t;
+      }
+      int nk = 0;
+      if (a == 0) {
+        p.seed_len[b] = 1;
+        p.seed_rows[2 * b] = 0;
+        p.seed_tokens[2 * b] = bonus;
+        p.seed_rows[2 * b + 1] = -1;
+        p.seed_tokens[2 * b + 1] = -1;
+      } else if (p.t_slot[ob + s_acc[a - 1]] >= 0) {
+        for (int i = 0; i < a; ++i) s_kept[nk++] = s_acc[i];
+        p.seed_len[b] = 1;
+        p.seed_rows[2 * b] = s_acc[a - 1];
+        p.seed_tokens[2 * b] = bonus;
+        p.seed_rows[2 * b + 1] = -1;
+        p.seed_tokens[2 * b + 1] = -1;
+      } else {
+        for (int i = 0; i < a - 1; ++i) s_kept[nk++] = s_acc[i];
+        p.seed_len[b] = 2;
+        p.seed_rows[2 * b] = a >= 2 ? s_acc[a - 2] : 0;
+        p.seed_tokens[2 * b] = p.t_token[ob + s_acc[a - 1]];
+        p.seed_rows[2 * b + 1] = s_acc[a - 1];
+        p.seed_tokens[2 * b + 1] = bonus;
+      }
+      s_nkept = nk;
+    }
+  }
+  __syncthreads();
+  if (p.kc == nullptr) return;
+  const int nk = s_nkept;
+  if (tid == 0) p.kv_len[b] = len_out + nk;
+  if (nk == 0) return;
+  // gather every kept row first, then scatter: destinations can overlap
+  // sources of other kept rows
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
+  const int n16 = p.hd * p.elem_bytes / 2;  // 16-bit units per row
+  for (int kvh = 0; kvh < p.nkv; ++kvh) {
+    for (int which = 0; which < 2; ++which) {
+      uint16_t* cache = static_cast<uint16_t*>(which ? p.vc : p.kc);
+      const int64_t hb = (static_cast<int64_t>(b) * p.nkv + kvh) * p.cap;
+      for (int e = tid; e < nk * n16; e += 256) {
+        const int i = e / n16, off = e % n16;
+        const int src = len_out + p.t_slot[ob + s_kept[i]];
+        s_rows[e] = (src >= 0 && src < p.cap) ? cache[(hb + src) * n16 + off] : 0;
+      }
+      __syncthreads();
+      for (int e = tid; e < nk * n16; e += 256) {
+        const int i = e / n16, off = e % n16;
+        const int dst = p_root + p.t_depth[ob + s_kept[i]];
+        if (dst >= 0 && dst < p.cap) cache[(hb + dst) * n16 + off] = s_rows[e];
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(row_stats_kernel, dim3(p.N + 1, p.batch), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = static_cast<size_t>(p.D) * p.hd * p.elem_bytes;
+  hipLaunchKernelGGL(walk_kernel, dim3(p.batch), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                     dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace eagle

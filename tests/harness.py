@@ -1,0 +1,154 @@
+"""Parity harness: seeded inputs fed to both the oracle and the HIP library.
+
+Inputs come from `synth`; they are rounded to the drafter's storage type by
+torch and the oracle receives exactly the stored values.  A sequence whose
+tree decisions have a score margin below 1e-3 (the oracle decides) is redrawn
+with the next attempt index."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+
+MARGIN = 1e-3
+
+
+def tol(cfg):
+    return (2e-2, 2e-2) if cfg.dtype == "bf16" else (1e-4, 1e-4)
+
+
+def tdtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def stored(cfg, arr) -> torch.Tensor:
+    """numpy float32 -> torch tensor in the storage type (CPU)."""
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(tdtype(cfg))
+
+
+def as_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def shape_of(cfg, max_batch=None, **kw):
+    from eagle_draft_tree_amd import DrafterShape
+    return DrafterShape(hidden=cfg.H, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv,
+                        head_dim=cfg.hd, ffn=cfg.F, vocab=cfg.V, dtype=cfg.dtype,
+                        rope_theta=cfg.theta, depth=cfg.D, topk=cfg.K,
+                        budget=cfg.N, max_batch=max_batch or cfg.B,
+                        max_seed=cfg.s_max, rms_eps=cfg.eps, **kw)
+
+
+class Model:
+    """Weights in storage type on CPU/GPU plus the oracle's float64 copy."""
+
+    def __init__(self, cfg, seed=0, gpu=True):
+        self.cfg = cfg
+        w32 = synth.weights(cfg, seed)
+        self.cpu = {n: stored(cfg, a) for n, a in w32.items()}
+        del w32
+        self.oracle = O.Weights(cfg, {n: t.float().numpy()
+                                      for n, t in self.cpu.items()})
+        self.gpu = {n: t.cuda() for n, t in self.cpu.items()} if gpu else None
+
+    def drafter(self, max_batch=None):
+        from eagle_draft_tree_amd import Drafter
+        return Drafter(shape_of(self.cfg, max_batch), self.gpu)
+
+
+class Seq:
+    """One sequence's first-round inputs, with its oracle tree."""
+
+    def __init__(self, model: Model, b: int, ctx: int, cap: int, attempt: int,
+                 run_oracle=True, record=False):
+        cfg = model.cfg
+        self.b, self.ctx, self.cap, self.attempt = b, ctx, cap, attempt
+        s = synth.seq_inputs(cfg, b, attempt)
+        self.low, self.mid, self.high = (stored(cfg, s[k]) for k in
+                                         ("low", "mid", "high"))
+        self.token = s["token"]
+        kk, vv = synth.prefix_kv(cfg, b, ctx, attempt)
+        self.k = torch.zeros(cfg.n_kv, cap, cfg.hd, dtype=tdtype(cfg))
+        self.v = torch.zeros_like(self.k)
+        self.k[:, :ctx] = stored(cfg, kk)
+        self.v[:, :ctx] = stored(cfg, vv)
+        self.tree = self.info = self.kv = self.g = None
+        if run_oracle:
+            W = model.oracle
+            self.g = O.fuse(W, as_np(self.low), as_np(self.mid), as_np(self.high))
+            self.kv = O.DraftKV(as_np(self.k), as_np(self.v))
+            self.tree, self.info = O.draft_tree(W, self.kv, self.g, [self.token],
+                                                ctx, record=record)
+            self.margin = O.decision_margin(cfg, self.info)
+
+
+def make_seq(model, b, ctx, cap, run_oracle=True, record=False, max_attempts=50):
+    for attempt in range(max_attempts):
+        s = Seq(model, b, ctx, cap, attempt, run_oracle, record)
+        if not run_oracle or s.margin >= MARGIN:
+            return s
+    raise RuntimeError("no input draw met the decision margin")
+
+
+def cap_for(cfg, ctx_max, rounds=1):
+    extra = cfg.s_max + (cfg.D - 1) * cfg.K + rounds * (cfg.D + 2) + 64
+    return int(ctx_max + extra)
+
+
+def upload_batch(model, seqs, cap):
+    """KV caches, lengths and first-round seed arrays on the GPU."""
+    from eagle_draft_tree_amd import KVCache
+    cfg = model.cfg
+    B = len(seqs)
+    k = torch.stack([s.k for s in seqs]).cuda()
+    v = torch.stack([s.v for s in seqs]).cuda()
+    kv = KVCache(k, v, torch.tensor([s.ctx for s in seqs], dtype=torch.int32).cuda())
+    low = torch.stack([s.low for s in seqs]).cuda()
+    mid = torch.stack([s.mid for s in seqs]).cuda()
+    high = torch.stack([s.high for s in seqs]).cuda()
+    tok = torch.full((B, cfg.s_max), -1, dtype=torch.int32)
+    tok[:, 0] = torch.tensor([s.token for s in seqs], dtype=torch.int32)
+    seed_len = torch.ones(B, dtype=torch.int32)
+    return kv, (low, mid, high), tok.cuda(), seed_len.cuda()
+
+
+def gpu_tree_round(drafter, model, seqs, kv, feats, tok, seed_len):
+    """fuse + draft_tree on the GPU for the first round."""
+    cfg = model.cfg
+    B = len(seqs)
+    low, mid, high = feats
+    g = drafter.fuse(low, mid, high)
+    seed_src = torch.zeros(B, cfg.s_max, cfg.H, dtype=torch.float32, device="cuda")
+    seed_src[:, 0] = g
+    tree, len_out = drafter.draft_tree(seed_src, tok, seed_len, kv)
+    torch.cuda.synchronize()
+    return g, tree, len_out
+
+
+def tree_to_np(tree, b):
+    return {k: v[b].cpu().numpy() for k, v in tree.items()}
+
+
+def assert_tree_equal(cfg, got, want):
+    """Bit-exact topology, tokens, slots, masks; scores within tolerance."""
+    n = int(want["n_nodes"])
+    assert int(got["n_nodes"]) == n
+    for k in ("token", "parent", "depth", "position", "kv_slot", "first_child",
+              "n_child"):
+        assert np.array_equal(got[k], want[k]), (k, got[k], want[k])
+    gm = got["mask"].astype(np.uint64)
+    assert np.array_equal(gm, want["mask"]), "mask"
+    atol, rtol = tol(cfg)
+    np.testing.assert_allclose(got["score"], want["score"], atol=atol, rtol=rtol)
+
+
+def target_logits(model, seq, rnd=0, attempt=0):
+    """Oracle draft logits at every tree row + N(0, 2^2) noise (float32)."""
+    cfg = model.cfg
+    base = O.score_rows(model.oracle, seq.kv, seq.tree, seq.info)
+    noise = synth.target_noise(cfg, seq.b, rnd, cfg.N + 1, attempt)
+    out = (base.astype(np.float64) + noise).astype(np.float32)
+    out[seq.tree["n_nodes"] + 1:] = 0.0
+    return out

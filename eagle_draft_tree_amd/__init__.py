@@ -114,6 +114,25 @@ class Drafter:
             pass
 
     # ------------------------------------------------------------------
+    def profile(self, on: bool):
+        check(lib().eagle_profile(self._ctx, 1 if on else 0), "eagle_profile")
+
+    def profile_read(self) -> dict:
+        import numpy as np
+        n = len(_lib.PROFILE_CLASSES)
+        ms = np.zeros(n, np.float32)
+        cnt = np.zeros(n, np.int32)
+        by = np.zeros(n, np.float64)
+        fl = np.zeros(n, np.float64)
+        check(lib().eagle_profile_read(
+            self._ctx, n, ms.ctypes.data_as(ctypes.c_void_p),
+            cnt.ctypes.data_as(ctypes.c_void_p),
+            by.ctypes.data_as(ctypes.c_void_p),
+            fl.ctypes.data_as(ctypes.c_void_p)), "eagle_profile_read")
+        return {name: {"ms": float(ms[i]), "launches": int(cnt[i]),
+                       "bytes": float(by[i]), "flops": float(fl[i])}
+                for i, name in enumerate(_lib.PROFILE_CLASSES)}
+
     def device_status(self) -> int:
         st = ctypes.c_int32(0)
         check(lib().eagle_get_device_status(self._ctx, ctypes.byref(st),

@@ -13,7 +13,9 @@ STATUS_NAMES = {0: "ok", 1: "invalid argument", 2: "unsupported shape",
                 5: "non-finite target logits", 6: "workspace too small"}
 EXPORTS = ("eagle_workspace_bytes", "eagle_create", "eagle_destroy",
            "eagle_status_str", "eagle_get_device_status", "eagle_fuse_features",
-           "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree")
+           "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree",
+           "eagle_profile", "eagle_profile_read")
+PROFILE_CLASSES = ("gemm", "fuse", "attention", "merge", "tree", "verify")
 
 c_int32_p = ctypes.c_void_p
 vp = ctypes.c_void_p
@@ -90,6 +92,10 @@ def lib():
     L.eagle_verify_tree.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Tree),
                                     vp, ctypes.c_float, vp, ctypes.POINTER(KV),
                                     vp, vp, vp, vp, vp, vp, vp]
+    L.eagle_profile.restype = ctypes.c_int
+    L.eagle_profile.argtypes = [vp, ctypes.c_int32]
+    L.eagle_profile_read.restype = ctypes.c_int
+    L.eagle_profile_read.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp]
     _lib = L
     return L
 

@@ -134,12 +134,26 @@ Offsets make_layout(const eagle_config& c) {
 
 }  // namespace
 
+// Optional per-launch timing: HIP events around each kernel of a context.
+struct Profiler {
+  static constexpr int kPairs = 4096;
+  bool on = false;
+  int used = 0;
+  bool overflow = false;
+  hipEvent_t ev[2 * kPairs] = {};
+  int cls[kPairs] = {};
+  double bytes[kPairs] = {};
+  double flops[kPairs] = {};
+  bool created = false;
+};
+
 struct eagle_ctx {
   eagle_config cfg;
   eagle_weights w;
   char* ws;
   Offsets off;
   int num_cus;
+  Profiler prof;
   template <typename P> P* at(size_t o) const { return reinterpret_cast<P*>(ws + o); }
   int* cnt() const { return at<int>(off.cnt_gemm); }
   int* done() const { return at<int>(off.cnt_done); }
@@ -148,6 +162,29 @@ struct eagle_ctx {
 };
 
 namespace {
+
+// kernel classes reported by eagle_profile_read
+enum ProfClass { PC_GEMM = 0, PC_FUSE = 1, PC_ATTN = 2, PC_MERGE = 3, PC_TREE = 4,
+                 PC_VERIFY = 5, PC_COUNT = 6 };
+
+int prof_begin(eagle_ctx* c, int cls, double bytes, double flops, hipStream_t s) {
+  Profiler& p = c->prof;
+  if (!p.on) return -1;
+  if (p.used >= Profiler::kPairs) {
+    p.overflow = true;
+    return -1;
+  }
+  const int i = p.used++;
+  p.cls[i] = cls;
+  p.bytes[i] = bytes;
+  p.flops[i] = flops;
+  if (hipEventRecord(p.ev[2 * i], s) != hipSuccess) p.overflow = true;
+  return i;
+}
+void prof_end(eagle_ctx* c, int i, hipStream_t s) {
+  if (i >= 0 && hipEventRecord(c->prof.ev[2 * i + 1], s) != hipSuccess)
+    c->prof.overflow = true;
+}
 
 struct Rows {  // one pass's query rows
   int batch, rps;
@@ -163,10 +200,13 @@ struct Rows {  // one pass's query rows
 };
 
 template <typename T>
-hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s) {
+hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEMM) {
   p.a_lo = 0;
-  if (sizeof(T) == 2)
-    for (int i = 0; i < p.nseg; ++i) p.a_lo |= p.seg[i].f32;
+  double a_bytes = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    if (sizeof(T) == 2) p.a_lo |= p.seg[i].f32;
+    a_bytes += static_cast<double>(p.M) * p.seg[i].width * (p.seg[i].f32 ? 4 : sizeof(T));
+  }
   p.Mtot = c->off.Rpad;
   p.part = c->at<float>(c->off.part);
   p.part_cols = 8 * c->off.nmax_part;
@@ -174,7 +214,14 @@ hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s) {
   p.done = c->done();
   p.eps = c->cfg.rms_eps;
   plan_gemm(p, c->num_cus);
-  return launch_gemm<T>(p, s);
+  // algorithmic bytes: weights once, activation rows in, results out
+  const double w_bytes = static_cast<double>(p.N) * p.K * sizeof(T);
+  const double out_bytes = p.epi == EPI_LMHEAD ? 0.0 : static_cast<double>(p.M) * p.N * 4;
+  const int pi = prof_begin(c, cls, w_bytes + a_bytes + out_bytes,
+                            2.0 * p.M * static_cast<double>(p.N) * p.K, s);
+  hipError_t e = launch_gemm<T>(p, s);
+  prof_end(c, pi, s);
+  return e;
 }
 
 template <typename T>
@@ -236,7 +283,9 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     p.part_o = c->at<float>(f.at_o); p.part_ml = c->at<float>(f.at_ml);
     p.cnt = c->attn_cnt();
     p.scale = 1.0f / sqrtf(static_cast<float>(cf.head_dim));
+    const int pi = prof_begin(c, PC_ATTN, 0.0, 0.0, s);
     EAGLE_TRY(launch_attention<T>(p, s));
+    prof_end(c, pi, s);
   }
   // a5 h = x + Wo o
   {
@@ -285,7 +334,9 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     m.rows = R; m.ntile = f.ntile_lm; m.topk = cf.topk;
     m.cand_val = p.cand_val; m.cand_id = p.cand_id; m.stat = p.stat;
     m.tok = r.tok; m.out_id = r.topk_id; m.out_val = r.topk_val; m.out_lse = r.lse;
+    const int pi = prof_begin(c, PC_MERGE, 0.0, 0.0, s);
     EAGLE_TRY(launch_merge(m, s));
+    prof_end(c, pi, s);
   }
 #undef EAGLE_TRY
   return EAGLE_OK;
@@ -334,7 +385,11 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
   sp.seed_token = seed_token; sp.seed_len = seed_len; sp.len_in = kv->len_in;
   sp.len_out = kv->len_out; sp.q = desc_of(c, 0);
   sp.sbase = c->at<int32_t>(f.sbase); sp.ts = tree_state(c); sp.status = c->status();
-  if (launch_seed_setup(sp, s) != hipSuccess) return EAGLE_EHIP;
+  {
+    const int pi = prof_begin(c, PC_TREE, 0.0, 0.0, s);
+    if (launch_seed_setup(sp, s) != hipSuccess) return EAGLE_EHIP;
+    prof_end(c, pi, s);
+  }
 
   const int passes = (D == 0 || N == 0) ? 1 : D;
   for (int d = 1; d <= passes; ++d) {
@@ -366,7 +421,9 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
     g.t_pos = out->position; g.t_slot = out->kv_slot; g.t_first = out->first_child;
     g.t_nchild = out->n_child; g.t_score = out->score; g.t_mask = out->mask;
     g.t_n = out->n_nodes; g.mask_words = (N + 1 + 63) / 64;
+    const int pi = prof_begin(c, PC_TREE, 0.0, 0.0, s);
     if (launch_grow(g, s) != hipSuccess) return EAGLE_EHIP;
+    prof_end(c, pi, s);
   }
   return EAGLE_OK;
 }
@@ -421,7 +478,12 @@ eagle_status eagle_create(const eagle_config* cfg, const eagle_weights* w,
   return EAGLE_OK;
 }
 
-void eagle_destroy(eagle_ctx* ctx) { delete ctx; }
+void eagle_destroy(eagle_ctx* ctx) {
+  if (ctx == nullptr) return;
+  if (ctx->prof.created)
+    for (int i = 0; i < 2 * Profiler::kPairs; ++i) (void)hipEventDestroy(ctx->prof.ev[i]);
+  delete ctx;
+}
 
 const char* eagle_status_str(eagle_status s) {
   switch (s) {
@@ -473,8 +535,8 @@ eagle_status eagle_fuse_features(eagle_ctx* ctx, int32_t rows, const void* low,
     p.epi = EPI_STORE;
     p.out = static_cast<float*>(g_out) + static_cast<size_t>(r0) * H;
     p.ldo = H;
-    hipError_t e = ctx->cfg.dtype == EAGLE_BF16 ? run_gemm<uint16_t>(ctx, p, stream)
-                                                : run_gemm<float>(ctx, p, stream);
+    hipError_t e = ctx->cfg.dtype == EAGLE_BF16 ? run_gemm<uint16_t>(ctx, p, stream, PC_FUSE)
+                                                : run_gemm<float>(ctx, p, stream, PC_FUSE);
     if (e != hipSuccess) return EAGLE_EHIP;
   }
   return EAGLE_OK;
@@ -558,7 +620,55 @@ eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* 
   p.kv_len = kv_or_null ? kv_or_null->len_out : nullptr;
   p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.elem_bytes = esize(cf);
   p.status = ctx->status();
-  return launch_verify(p, stream) == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+  const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * cf.vocab * 4.0;
+  const int pi = prof_begin(ctx, PC_VERIFY, vbytes, 0.0, stream);
+  const hipError_t e = launch_verify(p, stream);
+  prof_end(ctx, pi, stream);
+  return e == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+}
+
+eagle_status eagle_profile(eagle_ctx* ctx, int32_t on) {
+  if (ctx == nullptr) return EAGLE_EINVAL;
+  Profiler& p = ctx->prof;
+  if (on && !p.created) {
+    for (int i = 0; i < 2 * Profiler::kPairs; ++i)
+      if (hipEventCreate(&p.ev[i]) != hipSuccess) return EAGLE_EHIP;
+    p.created = true;
+  }
+  p.on = on != 0;
+  p.used = 0;
+  p.overflow = false;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_profile_read(eagle_ctx* ctx, int32_t n_classes, float* ms,
+                                int32_t* launches, double* bytes, double* flops) {
+  if (ctx == nullptr || ms == nullptr || launches == nullptr || bytes == nullptr ||
+      flops == nullptr || n_classes < 1)
+    return EAGLE_EINVAL;
+  Profiler& p = ctx->prof;
+  for (int k = 0; k < n_classes; ++k) {
+    ms[k] = 0.f;
+    launches[k] = 0;
+    bytes[k] = 0.0;
+    flops[k] = 0.0;
+  }
+  if (p.used > 0 && hipEventSynchronize(p.ev[2 * p.used - 1]) != hipSuccess)
+    return EAGLE_EHIP;
+  for (int i = 0; i < p.used; ++i) {
+    const int k = p.cls[i];
+    if (k >= n_classes) continue;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) return EAGLE_EHIP;
+    ms[k] += t;
+    launches[k] += 1;
+    bytes[k] += p.bytes[i];
+    flops[k] += p.flops[i];
+  }
+  const bool ovf = p.overflow;
+  p.used = 0;
+  p.overflow = false;
+  return ovf ? EAGLE_EWORKSPACE : EAGLE_OK;
 }
 
 }  // extern "C"

@@ -225,6 +225,21 @@ eagle_status eagle_verify_tree(eagle_ctx *ctx, int32_t batch,
                                int32_t *next_seed_tokens,
                                int32_t *next_seed_len, hipStream_t stream);
 
+/* Measurement hook.  While profiling is on, every kernel the context enqueues
+ * is bracketed by a pair of HIP events on its stream (up to 4096 launches
+ * between reads).  eagle_profile(ctx, 1) clears the record and starts;
+ * eagle_profile(ctx, 0) stops.  eagle_profile_read synchronises on the last
+ * event and returns, per kernel class, the summed event time (ms), launch
+ * count, algorithmic bytes (weights once + activations in/out; the target
+ * logits for verification) and algorithmic flops, then clears the record.
+ * Classes: 0 draft-layer GEMMs, 1 fusion GEMM, 2 tree attention, 3 LM-head
+ * top-k merge, 4 tree growth/rerank/flatten, 5 verification.  Returns
+ * EWORKSPACE if launches were dropped because the record was full. */
+eagle_status eagle_profile(eagle_ctx *ctx, int32_t on);
+eagle_status eagle_profile_read(eagle_ctx *ctx, int32_t n_classes, float *ms,
+                                int32_t *launches, double *bytes,
+                                double *flops);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ Parity pins for every function live in tests/test_oracle_*.py.
 """
 from __future__ import annotations
 
+import heapq
 import math
 
 import numpy as np
@@ -53,6 +54,8 @@ __all__ = [
     "fuse", "layer", "topk_desc", "lse32", "child_logprob", "DraftKV",
     "draft_tree", "select_key", "eagle2_tree", "flatten", "verify", "verify_row",
     "commit", "decision_margin", "score_rows", "causal_attention", "attend",
+    "philox4x64", "philox4x64_np", "uniform01", "verify_uniforms",
+    "STREAM_VERIFY", "STREAM_DRAFT", "BONUS_DRAW",
 ]
 
 # log of the confidence floor 1e-12 used for ranking ([M75] 0x06A), float32
@@ -259,66 +262,75 @@ def select_key(node):
     return (-float(node["score"]), node["depth"], node["id"])
 
 
+def _require_int(what: str, value, least: int):
+    if isinstance(value, bool) or not isinstance(value, int) or value < least:
+        raise ValueError(f"{what} has to be an int >= {least}, not {value!r}")
+
+
+def _make_children(parent, proposals, created: list) -> list:
+    """Append one parent's proposals to `created` as tree nodes.
+
+    A proposal is (token, float32 log confidence).  The record rules of
+    [M75] 0x06B are checked: a confidence is a probability (log <= 0, NaN
+    refused, log 0 of an impossible token allowed), a token occurs once per
+    parent, and the siblings' probabilities add up to at most one (1e-5 slack,
+    since they arrive as float32 logs).  Value of a child = parent value +
+    log(max(confidence, 1e-12)), accumulated in float32 ([M75] 0x06A)."""
+    toks = [t for t, _ in proposals]
+    logs = [np.float32(lc) for _, lc in proposals]
+    where = f"under node {parent['id']}"
+    if len(set(toks)) < len(toks):
+        raise ValueError(f"a token is proposed twice {where}")
+    if any(np.isnan(lc) or lc > np.float32(1e-6) for lc in logs):
+        raise ValueError(f"a log confidence {where} is not the log of a "
+                         f"probability: {[float(x) for x in logs]}")
+    mass = math.fsum(math.exp(float(lc)) for lc in logs)
+    if mass > 1.0 + 1e-5:
+        raise ValueError(f"children {where} carry probability {mass:.6f} > 1")
+    kids = []
+    for tok, lc in zip(toks, logs):
+        kids.append({"id": len(created), "token": tok, "parent": parent,
+                     "depth": parent["depth"] + 1, "slot": -1,
+                     "score": np.float32(parent["score"]
+                                         + max(lc, np.float32(LOG_EPS)))})
+        created.append(kids[-1])
+    return kids
+
+
 def eagle2_tree(root, expand, width: int, max_depth: int, budget: int):
-    """EAGLE-2 expansion and reranking ([M75] 0x06A-0x06B).
+    """EAGLE-2 dynamic tree ([M75] 0x06A-0x06B; [E3] 3.4 uses it with 10
+    nodes kept per step).
 
-    `root` is the seed node (depth 0, log value 0).  `expand(parents, depth)`
-    returns, for each parent (given in ascending node id), its children as
-    (token, log_confidence) pairs; log_confidence is float32 log p.  The value
-    of a node is the float32 sum of log(max(confidence, 1e-12)) along its path.
-    Each depth expands the `width` best nodes of the newest layer under the
-    order (-value, depth, node id); after `max_depth` expansions the `budget`
-    best nodes overall are returned.  Node ids follow creation order.
+    Growth goes one layer at a time.  Of the layer built last (at first: the
+    root alone), the `width` nodes that come first in the global order
+    (select_key) are handed to `expand(parents, depth)`, in ascending node id;
+    it returns, per parent, (token, float32 log confidence) proposals, which
+    become the next layer.  This repeats `max_depth` times.  Every node
+    created along the way stays a candidate, and the `budget` candidates that
+    come first in the global order are the tree.  Because a child's value
+    never exceeds its parent's and ties go to the shallower node, that set is
+    closed under ancestors.  A zero budget verifies nothing, so nothing is
+    drafted.  Node ids count creation order.
 
-    Raises ValueError on the argument and record violations the pages list:
-    width < 1, negative budget or depth, a confidence outside [0, 1], a
-    repeated token under one parent, sibling mass above one (tolerance 1e-5:
-    confidences arrive as float32 logs).  Returns (selected, all_nodes)."""
-    if type(width) is not int or width < 1:
-        raise ValueError("expansion width must be a positive integer")
-    for val in (budget, max_depth):
-        if type(val) is not int or val < 0:
-            raise ValueError("budget and depth must be nonnegative integers")
-    nodes = []
-    if budget == 0:
-        return [], nodes
-    frontier = [root]
-    for depth in range(max_depth):
-        if not frontier:
-            break
-        chosen = sorted(frontier, key=select_key)[:width]
-        chosen.sort(key=lambda n: n["id"])
-        kids = expand(chosen, depth)
-        nxt = []
-        for p, plist in zip(chosen, kids):
-            seen, mass = set(), 0.0
-            for tok, lc in plist:
-                lc = np.float32(lc)
-                conf = math.exp(float(lc))
-                if not math.isfinite(float(lc)) and float(lc) != -math.inf:
-                    raise ValueError("confidence must be a finite probability")
-                if not 0.0 <= conf <= 1.0 + 1e-6:
-                    raise ValueError("confidence must be a finite probability")
-                if tok in seen:
-                    raise ValueError("duplicate token under one parent")
-                seen.add(tok)
-                mass += conf
-                if mass > 1.0 + 1e-5:
-                    raise ValueError("sibling probability mass exceeds one")
-                c = {"id": len(nodes), "token": tok, "parent": p,
-                     "depth": p["depth"] + 1,
-                     "score": np.float32(p["score"]
-                                         + max(lc, np.float32(LOG_EPS))),
-                     "slot": -1}
-                nodes.append(c)
-                nxt.append(c)
-        frontier = nxt
-    selected = sorted(nodes, key=select_key)[:budget]
-    return selected, nodes
+    Argument and record errors raise ValueError (see _make_children).
+    Returns (selected nodes in global order, every created node)."""
+    _require_int("expansion width", width, 1)
+    _require_int("verification budget", budget, 0)
+    _require_int("maximum depth", max_depth, 0)
+    created = []
+    newest, depth = [root], 0
+    while newest and depth < max_depth and budget > 0:
+        parents = heapq.nsmallest(width, newest, key=select_key)
+        parents.sort(key=lambda n: n["id"])
+        proposals = expand(parents, depth)
+        newest = [kid for par, props in zip(parents, proposals)
+                  for kid in _make_children(par, props, created)]
+        depth += 1
+    return heapq.nsmallest(budget, created, key=select_key), created
 
 
 def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
-               record: bool = False):
+               record: bool = False, d2t=None):
     """Draft one tree for one sequence.
 
     Seed rows ([M75] 0x05A: [f_t, embed(x_{t+1})]) are appended to the draft
@@ -329,6 +341,12 @@ def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
     expanded at depth d >= 1 get scratch slot (d-1)*K + rank (rank in
     ascending node id) at cache index len_out + slot, position P_root + d, and
     see the committed prefix, their ancestors' slots and their own slot.
+
+    d2t: optional strictly increasing map from the drafter's reduced
+    vocabulary (the LM head's rows) to target token ids ([M75] 0x08C: the
+    draft head predicts over a configured sub-vocabulary with id maps).  Tree
+    tokens, the embedding lookups and verification then use target ids; the
+    map is increasing, so orders by draft id and by target id agree.
 
     Mutates kv (seed rows + scratch rows).  Returns (tree, info)."""
     cfg = W.cfg
@@ -355,8 +373,9 @@ def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
         for p in parents:
             lg = p["logits"]
             lse = lse32(lg)
-            res.append([(int(t), child_logprob(lg[t], lse))
-                        for t in sorted(int(i) for i in topk_desc(lg, K))])
+            ids = sorted(int(i) for i in topk_desc(lg, K))
+            res.append([(int(t) if d2t is None else int(d2t[t]),
+                         child_logprob(lg[t], lse)) for t in ids])
         return res
 
     def expand(chosen, depth):
@@ -510,6 +529,90 @@ def decision_margin(cfg, tree_info) -> float:
 
 
 # ---------------------------------------------------------------------------
+# counter-based random numbers: Philox4x64-10
+# ---------------------------------------------------------------------------
+# Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3"
+# (SC 2011): a 4 x 64-bit counter is encrypted under a 2 x 64-bit key by ten
+# rounds of two 64x64->128 multiplications; the key is bumped by two Weyl
+# constants between rounds.  Constants are the paper's for Philox4x64.
+PHILOX_MUL = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+PHILOX_WEYL = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+_M64 = (1 << 64) - 1
+
+# random streams of the key's second word
+STREAM_VERIFY = 0
+STREAM_DRAFT = 1
+# draw index of the residual (bonus) draw of a verified row
+BONUS_DRAW = 63
+
+
+def philox4x64(counter, key, rounds: int = 10):
+    """One Philox4x64 block, plain Python integers.  counter: 4 words,
+    key: 2 words.  Returns the 4 output words."""
+    x = [int(c) & _M64 for c in counter]
+    k0, k1 = int(key[0]) & _M64, int(key[1]) & _M64
+    for _ in range(rounds):
+        p0 = PHILOX_MUL[0] * x[0]
+        p1 = PHILOX_MUL[1] * x[2]
+        x = [(p1 >> 64) ^ x[1] ^ k0, p1 & _M64,
+             (p0 >> 64) ^ x[3] ^ k1, p0 & _M64]
+        k0 = (k0 + PHILOX_WEYL[0]) & _M64
+        k1 = (k1 + PHILOX_WEYL[1]) & _M64
+    return x
+
+
+def _mulhilo64(a, m: int):
+    """(high, low) 64-bit halves of a * m for a uint64 array, built from
+    32-bit limbs so that no intermediate exceeds 64 bits."""
+    a = a.astype(np.uint64)
+    mask = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    a_lo, a_hi = a & mask, a >> s32
+    m_lo, m_hi = np.uint64(m & 0xFFFFFFFF), np.uint64(m >> 32)
+    ll = a_lo * m_lo
+    lh = a_lo * m_hi
+    hl = a_hi * m_lo
+    hh = a_hi * m_hi
+    mid = (ll >> s32) + (lh & mask) + (hl & mask)
+    hi = hh + (lh >> s32) + (hl >> s32) + (mid >> s32)
+    return hi, a * np.uint64(m)
+
+
+def philox4x64_np(c0, c1, c2, c3, k0: int, k1: int):
+    """philox4x64 over uint64 arrays of counters (same rounds, vectorised)."""
+    x = [np.asarray(c, dtype=np.uint64).copy() for c in (c0, c1, c2, c3)]
+    with np.errstate(over="ignore"):
+        kk0, kk1 = np.uint64(k0 & _M64), np.uint64(k1 & _M64)
+        for _ in range(10):
+            h0, l0 = _mulhilo64(x[0], PHILOX_MUL[0])
+            h1, l1 = _mulhilo64(x[2], PHILOX_MUL[1])
+            x = [h1 ^ x[1] ^ kk0, l1, h0 ^ x[3] ^ kk1, l0]
+            kk0 = kk0 + np.uint64(PHILOX_WEYL[0])
+            kk1 = kk1 + np.uint64(PHILOX_WEYL[1])
+    return x
+
+
+def uniform01(seed: int, stream: int, rnd, b, row, draw) -> np.ndarray:
+    """U[0,1) float32 draws: counter (draw, row, b, round), key (seed,
+    stream); the top 24 bits of the block's first word, times 2^-24."""
+    shape = np.broadcast(np.asarray(rnd), np.asarray(b), np.asarray(row),
+                         np.asarray(draw)).shape
+    c = [np.broadcast_to(np.asarray(v, dtype=np.uint64), shape)
+         for v in (draw, row, b, rnd)]
+    x0 = philox4x64_np(*c, seed, stream)[0]
+    return ((x0 >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+def verify_uniforms(cfg, seed: int, rnd: int, b: int) -> np.ndarray:
+    """The [N+1, K+1] draws a verification of sequence b in round `rnd`
+    uses: column i < K for the i-th child of a row, column K the residual
+    draw (draw index BONUS_DRAW)."""
+    rows = np.arange(cfg.N + 1)[:, None]
+    draws = np.append(np.arange(cfg.K), BONUS_DRAW)[None, :]
+    return uniform01(seed, STREAM_VERIFY, rnd, b, rows, draws)
+
+
+# ---------------------------------------------------------------------------
 # (4) verification
 # ---------------------------------------------------------------------------
 def verify_row(logits, child_tokens, T: float, u_child, u_bonus):
@@ -562,16 +665,21 @@ def verify_row(logits, child_tokens, T: float, u_child, u_bonus):
     return None, tok, margin
 
 
-def verify(cfg, tree, target_logits, T: float, uniforms=None):
+def verify(cfg, tree, target_logits, T: float, uniforms=None, seed=None,
+           rnd: int = 0, b: int = 0):
     """Walk the flattened tree from the root ([E1] Algorithm 1, applied at
     each visited row; [E1] "The Full Inference Loop": a >= 0 accepted draft
     tokens plus one emitted token).
 
     target_logits [N+1, V] float32: row r holds the target's next-token
-    logits after node r.  uniforms [N+1, K+1]: column i < K is the draw for
-    the i-th child of that row (ascending token id), column K the bonus.
+    logits after node r.  The draws: `uniforms` [N+1, K+1] (column i < K for
+    the i-th child of that row in ascending token id, column K the residual
+    draw), or, when it is None, the Philox draws of (seed, round rnd,
+    sequence b) from verify_uniforms.
     Returns dict(accept_len, accepted_rows, tokens, bonus, margin)."""
     D, K = cfg.D, cfg.K
+    if uniforms is None and T > 0 and seed is not None:
+        uniforms = verify_uniforms(cfg, seed, rnd, b)
     v = 0
     acc = []
     margin = float("inf")
@@ -603,7 +711,7 @@ def verify(cfg, tree, target_logits, T: float, uniforms=None):
 # ---------------------------------------------------------------------------
 # commit of the accepted path ([M75] 0x05D)
 # ---------------------------------------------------------------------------
-def commit(cfg, tree, result, kv: DraftKV):
+def commit(cfg, tree, result, kv: DraftKV, mode: str = "keep"):
     """Publish the accepted path into the draft KV and build the next seed.
 
     [M75] 0x05D commits accepted state, discards unaccepted tree rows and
@@ -611,20 +719,33 @@ def commit(cfg, tree, result, kv: DraftKV):
     row maps come from the flatten metadata, never from token equality.
 
     Draft row of node u (depth i) sits at position P_root + i and was computed
-    from (parent state, token of u).  Accepted nodes u_1..u_{a-1} each have a
-    child in the tree, so each was expanded and owns a scratch row; u_a owns
-    one only if it was expanded.  Kept rows move to cache index = position.
-    The next seed supplies the missing rows with real target features:
+    from (parent state, token of u).  (row r, tok) below means "fused target
+    feature at flattened row r, joined with token tok"; the next draft call
+    appends such seed rows at the returned length.
+
+    mode "keep": accepted nodes u_1..u_{a-1} each have a child in the tree, so
+    each was expanded and owns a scratch row; u_a owns one only if it was
+    expanded.  Kept rows move to cache index = position, and the seed supplies
+    only the rows still missing:
       a == 0:                     [(row 0, bonus)]
       u_a expanded:               [(row u_a, bonus)]
       u_a not expanded:           [(row u_{a-1}, token u_a), (row u_a, bonus)]
-    where (row r, tok) means "fused target feature at flattened row r, joined
-    with token tok".  Returns (new_len, seed_rows, seed_tokens)."""
+    mode "reseed" ([E3] 3.4 Stage 2: the target's l, m, h at every verified
+    position are fused for the next round): no draft row is kept; the seed is
+    all a + 1 verified rows, [(row 0, tok u_1), (row u_1, tok u_2), ...,
+    (row u_a, bonus)].
+    Returns (new_len, seed_rows, seed_tokens)."""
     a = result["accept_len"]
     rows = list(result["accepted_rows"][:a])
     p_root = int(tree["position"][0])
     len_out = p_root + 1
     bonus = int(result["bonus"])
+    if mode == "reseed":
+        path = [0] + rows
+        nxt = [int(tree["token"][r]) for r in rows] + [bonus]
+        return len_out, path, nxt
+    if mode != "keep":
+        raise ValueError(mode)
     if a == 0:
         keep, seed = [], [(0, bonus)]
     elif tree["kv_slot"][rows[-1]] >= 0:

@@ -331,3 +331,104 @@ def test_commit_equals_explicit_concatenation(case):
         assert seed_rows == [prev, path[-1]]
         assert seed_toks == [int(tree["token"][path[-1]]), 17]
     assert n == cfg.N
+
+
+def test_sampling_law_under_seeded_philox_draws():
+    """The same whole-tree law, with every draw taken from the counter-based
+    generator: round i of seed 2024 drives the i-th verification."""
+    rng = np.random.default_rng(12)
+    cfg, tree = _hand_tree(5, 2, 2, [-1, 0, 0, 1, 1], [4, 1, 3, 0, 2])
+    V, T = 5, 0.7
+    lg = (rng.standard_normal((cfg.N + 1, V)) * 1.5).astype(np.float32)
+    p_rows = []
+    for r in range(cfg.N + 1):
+        w = np.exp((lg[r].astype(np.float64) - lg[r].max()) / T)
+        p_rows.append(w / w.sum())
+    law = _tree_law(tree, p_rows, 2)
+    n = 40000
+    draws = np.append(np.arange(cfg.K), O.BONUS_DRAW)
+    U = O.uniform01(2024, O.STREAM_VERIFY, np.arange(n)[:, None, None], 3,
+                    np.arange(cfg.N + 1)[None, :, None], draws[None, None, :])
+    counts = {}
+    for i in range(n):
+        r = O.verify(cfg, tree, lg, T, U[i])
+        key = tuple(int(x) for x in r["tokens"][: r["accept_len"] + 1])
+        counts[key] = counts.get(key, 0) + 1
+    # the seeded entry point draws exactly these numbers
+    for i in (0, 17, n - 1):
+        a = O.verify(cfg, tree, lg, T, seed=2024, rnd=i, b=3)
+        b = O.verify(cfg, tree, lg, T, U[i])
+        assert list(a["tokens"]) == list(b["tokens"])
+    from scipy.stats import chisquare
+    keys = sorted(law)
+    obs = np.array([counts.get(k, 0) for k in keys], dtype=np.float64)
+    exp = np.array([law[k] * n for k in keys])
+    stat, pval = chisquare(obs, exp)
+    assert pval > 1e-4, (stat, pval)
+
+
+@pytest.mark.parametrize("case", ["none", "leaf_last"])
+def test_reseed_commit_keeps_nothing_and_seeds_every_verified_row(case):
+    """Full reseed: no draft row survives; the next seed pairs every verified
+    row's target feature with the token that follows it, and the next draft
+    call appends them at the root's position + 1."""
+    cfg, W, kv, g, tok, P = _tiny_setup(D=3, K=2, N=6)
+    tree, info = O.draft_tree(W, kv, g, [tok], P)
+    kv_before = kv.copy()
+    path = []
+    if case != "none":
+        v = 0
+        while tree["n_child"][v] > 0:
+            v = int(tree["first_child"][v] + tree["n_child"][v] - 1)
+            path.append(v)
+    a = len(path)
+    res = {"accept_len": a,
+           "accepted_rows": np.array(path + [-1] * (cfg.D - a)),
+           "bonus": 21}
+    new_len, rows, toks = O.commit(cfg, tree, res, kv, mode="reseed")
+    assert new_len == P + 1
+    assert rows == [0] + path
+    assert toks == [int(tree["token"][r]) for r in path] + [21]
+    assert np.array_equal(kv.k, kv_before.k)
+    # the next round's seed rows land at P+1.. and see the prefix causally
+    feats = np.stack([g[0] * (1 + 0.1 * i) for i in range(len(rows))])
+    kv2 = kv.copy()
+    tree2, info2 = O.draft_tree(W, kv2, feats, toks, new_len)
+    assert info2["len_out"] == new_len + len(rows)
+    assert tree2["position"][0] == new_len + len(rows) - 1
+    kv3 = kv.copy()
+    ref = O.layer(W, kv3, feats, toks, pos=np.arange(new_len, new_len + len(rows)),
+                  dest=np.arange(new_len, new_len + len(rows)),
+                  visible=[np.arange(new_len + i + 1) for i in range(len(rows))])
+    lo, hi = new_len, new_len + len(rows)
+    assert np.array_equal(kv2.k[:, lo:hi], kv3.k[:, lo:hi])
+    assert np.array_equal(info2["root"]["a"], ref["a"][-1])
+
+
+def test_reduced_vocabulary_map():
+    """With an increasing draft->target id map d2t and a target embedding
+    whose row d2t[i] equals the draft table's row i, the tree is the unmapped
+    tree with every token sent through d2t."""
+    cfg, W, kv, g, tok, P = _tiny_setup(D=3, K=3, N=8)
+    kv0 = kv.copy()
+    tree0, _ = O.draft_tree(W, kv0, g, [tok], P)
+    V = cfg.V
+    d2t = np.arange(V) * 3 + 1
+    Vt = int(d2t[-1]) + 5
+    rng = np.random.default_rng(3)
+    Et = rng.standard_normal((Vt, cfg.H)) * 0.02
+    Et[d2t] = W.embed
+    W2 = O.Weights(cfg, {n: getattr(W, n) for n in O.Weights.NAMES})
+    W2.embed = Et
+    kv1 = kv.copy()
+    root_tok = int(d2t[tok])
+    tree1, _ = O.draft_tree(W2, kv1, g, [root_tok], P, d2t=d2t)
+    n = tree0["n_nodes"]
+    assert tree1["n_nodes"] == n
+    for k in ("parent", "depth", "position", "kv_slot", "first_child",
+              "n_child"):
+        assert np.array_equal(tree1[k], tree0[k]), k
+    assert np.array_equal(tree1["score"], tree0["score"])
+    assert list(tree1["token"][1:n + 1]) == list(d2t[tree0["token"][1:n + 1]])
+    assert tree1["token"][0] == root_tok
+    assert np.array_equal(kv1.k, kv0.k)

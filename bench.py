@@ -135,7 +135,7 @@ class Workload:
         self.d.fuse(*self.taps, out=g)
         self.d.draft_tree(self.seed_src, self.tok, self.seed_len, self.kv,
                           len_out=self.len_out, tree=self.tree)
-        self.res = self.d.verify(self.tree, self.logits, cfg.T, self.uniforms,
+        self.res = self.d.verify(self.tree, self.logits, cfg.T, seed=1, round=0,
                                  kv=self.kv, kv_len_out=self.kv_len, out=self.res)
 
     def run(self, steps, warmup):

@@ -16,7 +16,9 @@ from . import _lib
 from ._lib import EagleError, check, lib
 
 __all__ = ["DrafterShape", "Drafter", "KVCache", "EagleError", "lib",
-           "WEIGHT_NAMES"]
+           "WEIGHT_NAMES", "draw_uniforms", "COMMIT_KEEP", "COMMIT_RESEED"]
+
+COMMIT_KEEP, COMMIT_RESEED = _lib.COMMIT_KEEP, _lib.COMMIT_RESEED
 
 WEIGHT_NAMES = ("w_fuse", "w_in", "embed", "wq", "wk", "wv", "wo", "w_gate",
                 "w_up", "w_down", "w_lm", "g_attn", "g_mlp", "g_final")
@@ -38,6 +40,7 @@ class DrafterShape:
     max_batch: int
     max_seed: int = 2
     rms_eps: float = 1e-5
+    target_vocab: int = 0   # 0: same as vocab; larger needs a d2t map
 
     @property
     def torch_dtype(self):
@@ -49,7 +52,7 @@ class DrafterShape:
                            0 if self.dtype == "bf16" else 1,
                            float(self.rope_theta), float(self.rms_eps),
                            self.depth, self.topk, self.budget, self.max_batch,
-                           self.max_seed)
+                           self.max_seed, self.target_vocab)
 
 
 def _ptr(t):
@@ -94,7 +97,13 @@ class Drafter:
             if t.dtype != shape.torch_dtype or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"weight {n}: need contiguous {shape.torch_dtype} on GPU")
             self.weights[n] = t
-        self._w = _lib.Weights(*[self.weights[n].data_ptr() for n in WEIGHT_NAMES])
+        d2t = weights.get("d2t")
+        if d2t is not None:
+            if d2t.dtype != torch.int32 or not d2t.is_contiguous() or not d2t.is_cuda:
+                raise ValueError("d2t: need a contiguous int32 tensor on GPU")
+            self.weights["d2t"] = d2t
+        self._w = _lib.Weights(*[self.weights[n].data_ptr() for n in WEIGHT_NAMES],
+                               None if d2t is None else d2t.data_ptr())
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         ctx = ctypes.c_void_p()
         check(L.eagle_create(ctypes.byref(self._cfg), ctypes.byref(self._w),
@@ -205,18 +214,22 @@ class Drafter:
                                      _stream()), "eagle_draft_tree")
         return tree, len_out
 
-    def verify(self, tree, target_logits, temperature=0.0, uniforms=None,
-               kv: KVCache | None = None, kv_len_out=None, out=None):
+    def verify(self, tree, target_logits, temperature=0.0, seed=0, round=0,
+               kv: KVCache | None = None, kv_len_out=None, out=None,
+               commit_mode=_lib.COMMIT_KEEP, uniforms=None):
+        """Verify the trees; draws come from Philox(seed, round) unless
+        explicit `uniforms` [B, N+1, K+1] are given."""
         B = tree["token"].shape[0]
         D = self.shape.depth
+        S = self.shape.max_seed
         dev = target_logits.device
         i32 = dict(dtype=torch.int32, device=dev)
         if out is None:
             out = {"accept_len": torch.empty(B, **i32),
                    "accepted_rows": torch.empty(B, D, **i32),
                    "tokens": torch.empty(B, D + 1, **i32),
-                   "seed_rows": torch.empty(B, 2, **i32),
-                   "seed_tokens": torch.empty(B, 2, **i32),
+                   "seed_rows": torch.empty(B, S, **i32),
+                   "seed_tokens": torch.empty(B, S, **i32),
                    "seed_len": torch.empty(B, **i32)}
         ckv = None
         if kv is not None:
@@ -225,12 +238,27 @@ class Drafter:
             out["kv_len"] = kv_len_out
             ckv = kv.c_kv(None, kv_len_out)
         ct = self._c_tree(tree)
-        check(lib().eagle_verify_tree(
-            self._ctx, B, ctypes.byref(ct), _ptr(target_logits),
-            float(temperature), _ptr(uniforms),
-            ctypes.byref(ckv) if ckv is not None else None,
-            _ptr(out["accept_len"]), _ptr(out["accepted_rows"]),
-            _ptr(out["tokens"]), _ptr(out["seed_rows"]),
-            _ptr(out["seed_tokens"]), _ptr(out["seed_len"]), _stream()),
-            "eagle_verify_tree")
+        common = (_ptr(out["accept_len"]), _ptr(out["accepted_rows"]),
+                  _ptr(out["tokens"]), _ptr(out["seed_rows"]),
+                  _ptr(out["seed_tokens"]), _ptr(out["seed_len"]), _stream())
+        kvp = ctypes.byref(ckv) if ckv is not None else None
+        if uniforms is None:
+            check(lib().eagle_verify_tree(
+                self._ctx, B, ctypes.byref(ct), _ptr(target_logits),
+                float(temperature), int(seed), int(round), int(commit_mode),
+                kvp, *common), "eagle_verify_tree")
+        else:
+            check(lib().eagle_verify_tree_uniforms(
+                self._ctx, B, ctypes.byref(ct), _ptr(target_logits),
+                float(temperature), _ptr(uniforms), int(commit_mode), kvp,
+                *common), "eagle_verify_tree_uniforms")
         return out
+
+
+def draw_uniforms(seed, stream_id, round, batch, rows, draws, device="cuda"):
+    """U[0,1) draws [batch, rows, draws] of the library's Philox generator."""
+    out = torch.empty(batch, rows, draws, dtype=torch.float32, device=device)
+    check(lib().eagle_draw_uniforms(int(seed), int(stream_id), int(round), batch,
+                                    rows, draws, _ptr(out), _stream()),
+          "eagle_draw_uniforms")
+    return out

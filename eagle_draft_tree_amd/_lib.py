@@ -14,7 +14,10 @@ STATUS_NAMES = {0: "ok", 1: "invalid argument", 2: "unsupported shape",
 EXPORTS = ("eagle_workspace_bytes", "eagle_create", "eagle_destroy",
            "eagle_status_str", "eagle_get_device_status", "eagle_fuse_features",
            "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree",
+           "eagle_verify_tree_uniforms", "eagle_draw_uniforms",
            "eagle_profile", "eagle_profile_read")
+COMMIT_KEEP, COMMIT_RESEED = 0, 1
+STREAM_VERIFY, STREAM_DRAFT = 0, 1
 PROFILE_CLASSES = ("gemm", "fuse", "attention", "merge", "tree", "verify")
 
 c_int32_p = ctypes.c_void_p
@@ -28,13 +31,14 @@ class Config(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("depth", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("budget", ctypes.c_int32),
-                ("max_batch", ctypes.c_int32), ("max_seed", ctypes.c_int32)]
+                ("max_batch", ctypes.c_int32), ("max_seed", ctypes.c_int32),
+                ("target_vocab", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, vp) for n in (
         "w_fuse", "w_in", "embed", "wq", "wk", "wv", "wo", "w_gate", "w_up",
-        "w_down", "w_lm", "g_attn", "g_mlp", "g_final")]
+        "w_down", "w_lm", "g_attn", "g_mlp", "g_final", "d2t")]
 
 
 class KV(ctypes.Structure):
@@ -90,8 +94,18 @@ def lib():
                                    ctypes.POINTER(KV), ctypes.POINTER(Tree), vp]
     L.eagle_verify_tree.restype = ctypes.c_int
     L.eagle_verify_tree.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Tree),
-                                    vp, ctypes.c_float, vp, ctypes.POINTER(KV),
-                                    vp, vp, vp, vp, vp, vp, vp]
+                                    vp, ctypes.c_float, ctypes.c_uint64,
+                                    ctypes.c_uint64, ctypes.c_int32,
+                                    ctypes.POINTER(KV), vp, vp, vp, vp, vp, vp,
+                                    vp]
+    L.eagle_verify_tree_uniforms.restype = ctypes.c_int
+    L.eagle_verify_tree_uniforms.argtypes = [
+        vp, ctypes.c_int32, ctypes.POINTER(Tree), vp, ctypes.c_float, vp,
+        ctypes.c_int32, ctypes.POINTER(KV), vp, vp, vp, vp, vp, vp, vp]
+    L.eagle_draw_uniforms.restype = ctypes.c_int
+    L.eagle_draw_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
+                                      ctypes.c_uint64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, vp, vp]
     L.eagle_profile.restype = ctypes.c_int
     L.eagle_profile.argtypes = [vp, ctypes.c_int32]
     L.eagle_profile_read.restype = ctypes.c_int

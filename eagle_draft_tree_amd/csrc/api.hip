@@ -39,6 +39,8 @@ struct Offsets {
 };
 
 int esize(const eagle_config& c) { return c.dtype == EAGLE_BF16 ? 2 : 4; }
+// token ids of the tree, the embedding and the target logits
+int tvocab(const eagle_config& c) { return c.target_vocab > 0 ? c.target_vocab : c.vocab; }
 
 eagle_status check_config(const eagle_config* c) {
   if (c == nullptr) return EAGLE_EINVAL;
@@ -53,13 +55,15 @@ eagle_status check_config(const eagle_config* c) {
   if (c->hidden % 16 || c->ffn % 8 || c->vocab % 16) return EAGLE_EUNSUPPORTED;
   if (c->topk > kMaxTopK || c->vocab < c->topk) return EAGLE_EUNSUPPORTED;
   if (c->depth > 0 && (c->depth - 1) * c->topk > 64) return EAGLE_EUNSUPPORTED;
-  if (c->budget + 1 > 128 || c->max_seed > 4) return EAGLE_EUNSUPPORTED;
+  if (c->budget + 1 > 128 || c->max_seed > 16) return EAGLE_EUNSUPPORTED;
   const int rps = std::max(c->max_seed, c->topk);
   const int G = c->n_q_heads / c->n_kv_heads;
   if (rps * G > 128) return EAGLE_EUNSUPPORTED;
   if (c->dtype == EAGLE_FP32 && (c->max_batch * rps > 64 || c->head_dim != 64))
     return EAGLE_EUNSUPPORTED;
   if (c->max_batch > 4096) return EAGLE_EUNSUPPORTED;
+  if (c->target_vocab < 0) return EAGLE_EINVAL;
+  if (c->target_vocab != 0 && c->target_vocab < c->vocab) return EAGLE_EINVAL;
   return EAGLE_OK;
 }
 
@@ -246,7 +250,7 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     p.seg[0].base = r.src; p.seg[0].ld = H; p.seg[0].rowidx = r.src_row;
     p.seg[0].rowlimit = r.src_rows; p.seg[0].width = H;
     p.seg[1].base = c->w.embed; p.seg[1].ld = H; p.seg[1].rowidx = r.tok;
-    p.seg[1].rowlimit = V; p.seg[1].width = H; p.seg[1].f32 = 0;
+    p.seg[1].rowlimit = tvocab(cf); p.seg[1].width = H; p.seg[1].f32 = 0;
     p.w0 = c->w.w_in;
     p.epi = EPI_STORE; p.out = c->at<char>(f.x); p.ldo = H;
     p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rn1);
@@ -416,7 +420,7 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
     g.rows_per_seq = rps; g.s_max = cf.max_seed;
     g.topk_id = r.topk_id; g.topk_val = r.topk_val; g.lse = r.lse;
     g.cur = cur; g.nxt = nxt; g.ts = tree_state(c);
-    g.seed_token = seed_token; g.seed_len = seed_len;
+    g.seed_token = seed_token; g.seed_len = seed_len; g.d2t = c->w.d2t;
     g.t_token = out->token; g.t_parent = out->parent; g.t_depth = out->depth;
     g.t_pos = out->position; g.t_slot = out->kv_slot; g.t_first = out->first_child;
     g.t_nchild = out->n_child; g.t_score = out->score; g.t_mask = out->mask;
@@ -456,6 +460,22 @@ eagle_status eagle_create(const eagle_config* cfg, const eagle_weights* w,
   for (const void* p : ptrs)
     if (p == nullptr) return EAGLE_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return EAGLE_EINVAL;
+  if ((w->d2t == nullptr) != (cfg->target_vocab == 0 || cfg->target_vocab == cfg->vocab))
+    return EAGLE_EINVAL;
+  if (w->d2t != nullptr) {
+    // the map must be strictly increasing into [0, target_vocab)
+    int32_t* h = static_cast<int32_t*>(malloc(sizeof(int32_t) * cfg->vocab));
+    if (h == nullptr) return EAGLE_EINVAL;
+    if (hipStreamSynchronize(stream) != hipSuccess ||
+        hipMemcpy(h, w->d2t, sizeof(int32_t) * cfg->vocab, hipMemcpyDeviceToHost) != hipSuccess) {
+      free(h);
+      return EAGLE_EHIP;
+    }
+    bool ok = h[0] >= 0 && h[cfg->vocab - 1] < cfg->target_vocab;
+    for (int i = 1; i < cfg->vocab && ok; ++i) ok = h[i] > h[i - 1];
+    free(h);
+    if (!ok) return EAGLE_EINVAL;
+  }
   Offsets off = make_layout(*cfg);
   if (ws_bytes < off.total) return EAGLE_EWORKSPACE;
   int dev = 0, cus = 256;
@@ -584,13 +604,17 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_sr
                                       stream);
 }
 
-eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
-                               const float* target_logits, float temperature,
-                               const float* uniforms, const eagle_kv* kv_or_null,
-                               int32_t* accept_len, int32_t* accepted_rows,
-                               int32_t* out_tokens, int32_t* next_seed_rows,
-                               int32_t* next_seed_tokens, int32_t* next_seed_len,
-                               hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                         const float* target_logits, float temperature,
+                         const float* uniforms, uint64_t seed, uint64_t round,
+                         int32_t commit_mode, const eagle_kv* kv_or_null,
+                         int32_t* accept_len, int32_t* accepted_rows, int32_t* out_tokens,
+                         int32_t* next_seed_rows, int32_t* next_seed_tokens,
+                         int32_t* next_seed_len, hipStream_t stream) {
   if (ctx == nullptr || null_tree(tree)) return EAGLE_EINVAL;
   const eagle_config& cf = ctx->cfg;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
@@ -598,14 +622,20 @@ eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* 
   if (!target_logits || !accept_len || !accepted_rows || !out_tokens ||
       !next_seed_rows || !next_seed_tokens || !next_seed_len)
     return EAGLE_EINVAL;
-  if (temperature > 0.f && uniforms == nullptr) return EAGLE_EINVAL;
+  if (commit_mode != EAGLE_COMMIT_KEEP && commit_mode != EAGLE_COMMIT_RESEED)
+    return EAGLE_EINVAL;
+  // seed outputs hold max_seed slots per sequence: 2 for the keep policy,
+  // D + 1 for a full reseed
+  if (cf.max_seed < (commit_mode == EAGLE_COMMIT_RESEED ? cf.depth + 1 : 2))
+    return EAGLE_EUNSUPPORTED;
   if (kv_or_null && (!kv_or_null->k || !kv_or_null->v || !kv_or_null->len_out ||
                      kv_or_null->cap < 1))
     return EAGLE_EINVAL;
   const Offsets& f = ctx->off;
   VerifyParams p;
-  p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = cf.vocab;
+  p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = tvocab(cf);
   p.T = temperature; p.logits = target_logits; p.uniforms = uniforms;
+  p.seed = seed; p.round = round; p.commit_mode = commit_mode; p.S = cf.max_seed;
   p.t_token = tree->token; p.t_parent = tree->parent; p.t_depth = tree->depth;
   p.t_pos = tree->position; p.t_slot = tree->kv_slot; p.t_first = tree->first_child;
   p.t_nchild = tree->n_child; p.t_n = tree->n_nodes;
@@ -620,11 +650,51 @@ eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* 
   p.kv_len = kv_or_null ? kv_or_null->len_out : nullptr;
   p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.elem_bytes = esize(cf);
   p.status = ctx->status();
-  const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * cf.vocab * 4.0;
+  const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * p.V * 4.0;
   const int pi = prof_begin(ctx, PC_VERIFY, vbytes, 0.0, stream);
   const hipError_t e = launch_verify(p, stream);
   prof_end(ctx, pi, stream);
   return e == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                               const float* target_logits, float temperature,
+                               uint64_t seed, uint64_t round, int32_t commit_mode,
+                               const eagle_kv* kv_or_null, int32_t* accept_len,
+                               int32_t* accepted_rows, int32_t* out_tokens,
+                               int32_t* next_seed_rows, int32_t* next_seed_tokens,
+                               int32_t* next_seed_len, hipStream_t stream) {
+  return verify_impl(ctx, batch, tree, target_logits, temperature, nullptr, seed, round,
+                     commit_mode, kv_or_null, accept_len, accepted_rows, out_tokens,
+                     next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+eagle_status eagle_verify_tree_uniforms(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                                        const float* target_logits, float temperature,
+                                        const float* uniforms, int32_t commit_mode,
+                                        const eagle_kv* kv_or_null, int32_t* accept_len,
+                                        int32_t* accepted_rows, int32_t* out_tokens,
+                                        int32_t* next_seed_rows, int32_t* next_seed_tokens,
+                                        int32_t* next_seed_len, hipStream_t stream) {
+  if (temperature > 0.f && uniforms == nullptr) return EAGLE_EINVAL;
+  return verify_impl(ctx, batch, tree, target_logits, temperature, uniforms, 0, 0,
+                     commit_mode, kv_or_null, accept_len, accepted_rows, out_tokens,
+                     next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+eagle_status eagle_draw_uniforms(uint64_t seed, uint64_t stream_id, uint64_t round,
+                                 int32_t batch, int32_t rows, int32_t draws, float* out,
+                                 hipStream_t stream) {
+  if (batch < 0 || rows < 0 || draws < 0 || batch > 65535 || rows > 65535) return EAGLE_EINVAL;
+  if (batch == 0 || rows == 0 || draws == 0) return EAGLE_OK;
+  if (out == nullptr) return EAGLE_EINVAL;
+  return launch_uniforms(seed, stream_id, round, batch, rows, draws, out, stream) == hipSuccess
+             ? EAGLE_OK
+             : EAGLE_EHIP;
 }
 
 eagle_status eagle_profile(eagle_ctx* ctx, int32_t on) {

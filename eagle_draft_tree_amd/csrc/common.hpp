@@ -177,4 +177,41 @@ __device__ __forceinline__ void wave_sort_desc(float& v, int& id) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// ----------------------------------------------------------------------------
+// Philox4x64-10 counter-based generator (Salmon, Moraes, Dror, Shaw, SC 2011):
+// ten rounds of two 64x64->128-bit multiplications over a 4-word counter,
+// key bumped by two Weyl constants between rounds.
+// ----------------------------------------------------------------------------
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+constexpr uint64_t kStreamVerify = 0;   // key word 1 of verification draws
+constexpr uint64_t kStreamDraft = 1;    // key word 1 of drafting draws
+
+// first output word of the block at counter (c0, c1, c2, c3), key (k0, k1)
+__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                  uint64_t c3, uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return c0;
+}
+
+// U[0,1) float: counter (draw, row, sequence, round), key (seed, stream);
+// the top 24 bits of the first output word times 2^-24 (exact in float)
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t stream, uint64_t rnd,
+                                                uint64_t b, uint64_t row, uint64_t draw) {
+  const uint64_t x = philox4x64_w0(draw, row, b, rnd, seed, stream);
+  return static_cast<float>(x >> 40) * 5.9604644775390625e-08f;
+}
+
 }  // namespace eagle

@@ -133,6 +133,7 @@ hipError_t launch_seed_setup(const SeedParams& p, hipStream_t s);
 
 struct GrowParams {
   int batch, K, D, N, pass, rows_per_seq, s_max;
+  const int32_t* d2t;   // draft id -> target id, or null (same vocabulary)
   const int32_t* topk_id; const float* topk_val; const float* lse;
   QueryDesc cur;      // this pass's rows
   QueryDesc nxt;      // next pass's rows [B * K]
@@ -149,7 +150,10 @@ struct VerifyParams {
   int batch, N, K, D, V;
   float T;
   const float* logits;      // [B, N+1, V]
-  const float* uniforms;    // [B, N+1, K+1] or null
+  const float* uniforms;    // [B, N+1, K+1] or null: Philox draws of (seed, round)
+  uint64_t seed, round;
+  int commit_mode;          // 0 keep computed draft rows, 1 full reseed
+  int S;                    // seed slots per sequence in the seed outputs
   const int32_t *t_token, *t_parent, *t_depth, *t_pos, *t_slot, *t_first,
       *t_nchild, *t_n;
   float* row_max; double* row_sum; int32_t* row_arg; int32_t* row_bad;
@@ -162,5 +166,7 @@ struct VerifyParams {
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+hipError_t launch_uniforms(uint64_t seed, uint64_t stream, uint64_t rnd, int batch, int rows,
+                           int draws, float* out, hipStream_t s);
 
 }  // namespace eagle

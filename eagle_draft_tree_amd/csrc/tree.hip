@@ -7,6 +7,7 @@
 namespace eagle {
 
 constexpr int kMaxCand = 16 + 7 * 256;  // >= K + (D-1) K^2 when (D-1)K <= 64
+constexpr int kBonusDraw = 63;          // draw index of a row's residual draw
 constexpr int kMaxPath = 72;            // >= D + 1 when (D-1)K <= 64
 
 // ============================================================================
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
     const float ps = parent < 0 ? 0.f : ts.c_score[cb + parent];
     float lp = p.topk_val[static_cast<int64_t>(row) * K + cc] - p.lse[row];
     lp = fmaxf(lp, kLogEps);
-    ts.c_token[cb + node] = my;
+    ts.c_token[cb + node] = p.d2t != nullptr ? p.d2t[my] : my;
     ts.c_parent[cb + node] = parent;
     ts.c_depth[cb + node] = p.pass;
     ts.c_score[cb + node] = ps + lp;
@@ -407,6 +408,17 @@ __global__ __launch_bounds__(256) void row_stats_kernel(VerifyParams p) {
   }
 }
 
+// Draw j of flattened row v of sequence b: the caller's uniforms when given
+// (column j < K, or column K for the residual draw), else Philox.
+__device__ __forceinline__ float draw_uniform(const VerifyParams& p, int b, int v, int j) {
+  if (p.uniforms != nullptr) {
+    const int col = j == kBonusDraw ? p.K : j;
+    return p.uniforms[(static_cast<int64_t>(b) * (p.N + 1) + v) * (p.K + 1) + col];
+  }
+  return philox_uniform(p.seed, kStreamVerify, p.round, static_cast<uint64_t>(b),
+                        static_cast<uint64_t>(v), static_cast<uint64_t>(j));
+}
+
 __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
   __shared__ int s_kids[kMaxTopK];
   __shared__ int s_nk, s_row, s_need_res, s_bad, s_a, s_bonus;
@@ -425,8 +437,7 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
       for (int i = 0; i < p.D; ++i) p.accepted_rows[b * p.D + i] = -1;
       for (int i = 0; i <= p.D; ++i) p.out_tokens[b * (p.D + 1) + i] = -1;
       p.seed_len[b] = 0;
-      p.seed_rows[2 * b] = p.seed_rows[2 * b + 1] = -1;
-      p.seed_tokens[2 * b] = p.seed_tokens[2 * b + 1] = -1;
+      for (int i = 0; i < p.S; ++i) p.seed_rows[b * p.S + i] = p.seed_tokens[b * p.S + i] = -1;
     }
     return;
   }
@@ -450,14 +461,16 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
       } else {
         double S = p.row_sum[ob + v];
         const float mx = p.row_max[ob + v];
-        const float* u = p.uniforms + (ob + v) * (p.K + 1);
         for (int j = 0; j < nc; ++j) {
           const int tok = p.t_token[ob + fc + j];
+          if (tok < 0 || tok >= p.V) { bad = 1; break; }
           s_kids[j] = tok;
           const double w = static_cast<double>(wexp(lg[tok], mx, p.T));
-          if (static_cast<double>(u[j]) * S < w) { nxt = fc + j; break; }
+          const float u = draw_uniform(p, b, v, j);
+          if (static_cast<double>(u) * S < w) { nxt = fc + j; break; }
           S -= w;
         }
+        if (bad) break;
         if (nxt < 0) {
           need = 1;
           s_nk = nc;
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
     }
     const double total = s_part[255];
     const double excl = s_part[tid] - part;
-    const double u = static_cast<double>(p.uniforms[(ob + v) * (p.K + 1) + p.K]);
+    const double u = static_cast<double>(draw_uniform(p, b, v, kBonusDraw));
     const double thr = u * total;
     int pick = -1;
     if (total > 0.0) {
@@ -569,14 +582,15 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
   const int p_root = p.t_pos[ob];
   const int len_out = p_root + 1;
   if (tid == 0) {
+    int* srow = p.seed_rows + b * p.S;
+    int* stok = p.seed_tokens + b * p.S;
+    for (int i = 0; i < p.S; ++i) srow[i] = stok[i] = -1;
     if (bad) {
       atomicOr(p.status, 1 << 5);
       p.accept_len[b] = -1;
       for (int i = 0; i < p.D; ++i) p.accepted_rows[b * p.D + i] = -1;
       for (int i = 0; i <= p.D; ++i) p.out_tokens[b * (p.D + 1) + i] = -1;
       p.seed_len[b] = 0;
-      p.seed_rows[2 * b] = p.seed_rows[2 * b + 1] = -1;
-      p.seed_tokens[2 * b] = p.seed_tokens[2 * b + 1] = -1;
       s_nkept = 0;
     } else {
       const int bonus = s_bonus;
@@ -589,26 +603,29 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
         p.out_tokens[b * (p.D + 1) + i] = t;
       }
       int nk = 0;
-      if (a == 0) {
+      if (p.commit_mode == 1) {
+        // full reseed: every verified row's feature joins the next token
+        p.seed_len[b] = a + 1;
+        for (int i = 0; i <= a; ++i) {
+          srow[i] = i == 0 ? 0 : s_acc[i - 1];
+          stok[i] = i < a ? p.t_token[ob + s_acc[i]] : bonus;
+        }
+      } else if (a == 0) {
         p.seed_len[b] = 1;
-        p.seed_rows[2 * b] = 0;
-        p.seed_tokens[2 * b] = bonus;
-        p.seed_rows[2 * b + 1] = -1;
-        p.seed_tokens[2 * b + 1] = -1;
+        srow[0] = 0;
+        stok[0] = bonus;
       } else if (p.t_slot[ob + s_acc[a - 1]] >= 0) {
         for (int i = 0; i < a; ++i) s_kept[nk++] = s_acc[i];
         p.seed_len[b] = 1;
-        p.seed_rows[2 * b] = s_acc[a - 1];
-        p.seed_tokens[2 * b] = bonus;
-        p.seed_rows[2 * b + 1] = -1;
-        p.seed_tokens[2 * b + 1] = -1;
+        srow[0] = s_acc[a - 1];
+        stok[0] = bonus;
       } else {
         for (int i = 0; i < a - 1; ++i) s_kept[nk++] = s_acc[i];
         p.seed_len[b] = 2;
-        p.seed_rows[2 * b] = a >= 2 ? s_acc[a - 2] : 0;
-        p.seed_tokens[2 * b] = p.t_token[ob + s_acc[a - 1]];
-        p.seed_rows[2 * b + 1] = s_acc[a - 1];
-        p.seed_tokens[2 * b + 1] = bonus;
+        srow[0] = a >= 2 ? s_acc[a - 2] : 0;
+        stok[0] = p.t_token[ob + s_acc[a - 1]];
+        srow[1] = s_acc[a - 1];
+        stok[1] = bonus;
       }
       s_nkept = nk;
     }
@@ -648,6 +665,24 @@ hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const size_t lds = static_cast<size_t>(p.D) * p.hd * p.elem_bytes;
   hipLaunchKernelGGL(walk_kernel, dim3(p.batch), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+__global__ void uniforms_kernel(uint64_t seed, uint64_t stream, uint64_t rnd, int rows,
+                                int draws, float* out) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int r = blockIdx.y, b = blockIdx.z;
+  if (j >= draws) return;
+  out[(static_cast<int64_t>(b) * rows + r) * draws + j] =
+      philox_uniform(seed, stream, rnd, static_cast<uint64_t>(b), static_cast<uint64_t>(r),
+                     static_cast<uint64_t>(j));
+}
+
+hipError_t launch_uniforms(uint64_t seed, uint64_t stream, uint64_t rnd, int batch, int rows,
+                           int draws, float* out, hipStream_t s) {
+  if (batch <= 0 || rows <= 0 || draws <= 0) return hipSuccess;
+  hipLaunchKernelGGL(uniforms_kernel, dim3((draws + 255) / 256, rows, batch), dim3(256), 0, s,
+                     seed, stream, rnd, rows, draws, out);
   return hipGetLastError();
 }
 

@@ -34,11 +34,12 @@ def as_np(t: torch.Tensor) -> np.ndarray:
 
 def shape_of(cfg, max_batch=None, **kw):
     from eagle_draft_tree_amd import DrafterShape
+    kw.setdefault("max_seed", cfg.s_max)
     return DrafterShape(hidden=cfg.H, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv,
                         head_dim=cfg.hd, ffn=cfg.F, vocab=cfg.V, dtype=cfg.dtype,
                         rope_theta=cfg.theta, depth=cfg.D, topk=cfg.K,
                         budget=cfg.N, max_batch=max_batch or cfg.B,
-                        max_seed=cfg.s_max, rms_eps=cfg.eps, **kw)
+                        rms_eps=cfg.eps, **kw)
 
 
 class Model:
@@ -53,22 +54,22 @@ class Model:
                                       for n, t in self.cpu.items()})
         self.gpu = {n: t.cuda() for n, t in self.cpu.items()} if gpu else None
 
-    def drafter(self, max_batch=None):
+    def drafter(self, max_batch=None, **kw):
         from eagle_draft_tree_amd import Drafter
-        return Drafter(shape_of(self.cfg, max_batch), self.gpu)
+        return Drafter(shape_of(self.cfg, max_batch, **kw), self.gpu)
 
 
 class Seq:
     """One sequence's first-round inputs, with its oracle tree."""
 
     def __init__(self, model: Model, b: int, ctx: int, cap: int, attempt: int,
-                 run_oracle=True, record=False):
+                 run_oracle=True, record=False, d2t=None):
         cfg = model.cfg
         self.b, self.ctx, self.cap, self.attempt = b, ctx, cap, attempt
         s = synth.seq_inputs(cfg, b, attempt)
         self.low, self.mid, self.high = (stored(cfg, s[k]) for k in
                                          ("low", "mid", "high"))
-        self.token = s["token"]
+        self.token = s["token"] if d2t is None else int(d2t[s["token"]])
         kk, vv = synth.prefix_kv(cfg, b, ctx, attempt)
         self.k = torch.zeros(cfg.n_kv, cap, cfg.hd, dtype=tdtype(cfg))
         self.v = torch.zeros_like(self.k)
@@ -80,13 +81,14 @@ class Seq:
             self.g = O.fuse(W, as_np(self.low), as_np(self.mid), as_np(self.high))
             self.kv = O.DraftKV(as_np(self.k), as_np(self.v))
             self.tree, self.info = O.draft_tree(W, self.kv, self.g, [self.token],
-                                                ctx, record=record)
+                                                ctx, record=record, d2t=d2t)
             self.margin = O.decision_margin(cfg, self.info)
 
 
-def make_seq(model, b, ctx, cap, run_oracle=True, record=False, max_attempts=50):
+def make_seq(model, b, ctx, cap, run_oracle=True, record=False, max_attempts=50,
+             d2t=None):
     for attempt in range(max_attempts):
-        s = Seq(model, b, ctx, cap, attempt, run_oracle, record)
+        s = Seq(model, b, ctx, cap, attempt, run_oracle, record, d2t)
         if not run_oracle or s.margin >= MARGIN:
             return s
     raise RuntimeError("no input draw met the decision margin")
@@ -97,18 +99,19 @@ def cap_for(cfg, ctx_max, rounds=1):
     return int(ctx_max + extra)
 
 
-def upload_batch(model, seqs, cap):
+def upload_batch(model, seqs, cap, s_max=None):
     """KV caches, lengths and first-round seed arrays on the GPU."""
     from eagle_draft_tree_amd import KVCache
     cfg = model.cfg
     B = len(seqs)
+    S = s_max or cfg.s_max
     k = torch.stack([s.k for s in seqs]).cuda()
     v = torch.stack([s.v for s in seqs]).cuda()
     kv = KVCache(k, v, torch.tensor([s.ctx for s in seqs], dtype=torch.int32).cuda())
     low = torch.stack([s.low for s in seqs]).cuda()
     mid = torch.stack([s.mid for s in seqs]).cuda()
     high = torch.stack([s.high for s in seqs]).cuda()
-    tok = torch.full((B, cfg.s_max), -1, dtype=torch.int32)
+    tok = torch.full((B, S), -1, dtype=torch.int32)
     tok[:, 0] = torch.tensor([s.token for s in seqs], dtype=torch.int32)
     seed_len = torch.ones(B, dtype=torch.int32)
     return kv, (low, mid, high), tok.cuda(), seed_len.cuda()
@@ -120,7 +123,8 @@ def gpu_tree_round(drafter, model, seqs, kv, feats, tok, seed_len):
     B = len(seqs)
     low, mid, high = feats
     g = drafter.fuse(low, mid, high)
-    seed_src = torch.zeros(B, cfg.s_max, cfg.H, dtype=torch.float32, device="cuda")
+    seed_src = torch.zeros(B, drafter.shape.max_seed, cfg.H, dtype=torch.float32,
+                           device="cuda")
     seed_src[:, 0] = g
     tree, len_out = drafter.draft_tree(seed_src, tok, seed_len, kv)
     torch.cuda.synchronize()
@@ -152,3 +156,90 @@ def target_logits(model, seq, rnd=0, attempt=0):
     out = (base.astype(np.float64) + noise).astype(np.float32)
     out[seq.tree["n_nodes"] + 1:] = 0.0
     return out
+
+
+# ---------------------------------------------------------------------------
+# chained rounds: verify -> commit -> fuse next seed -> draft, oracle side
+# ---------------------------------------------------------------------------
+SEED = 20240917        # Philox key word 0 of every verification in the tests
+
+
+def target_logits_for(model, tree, info, kv, b, rnd, attempt=0, d2t=None,
+                      target_vocab=None):
+    """Oracle draft logits at every tree row + N(0, 2^2) noise (float32),
+    spread over the target vocabulary when a reduced draft vocabulary is in
+    use (rows outside the draft vocabulary get noise only)."""
+    cfg = model.cfg
+    base = O.score_rows(model.oracle, kv, tree, info)
+    TV = target_vocab or cfg.V
+    noise = synth.normal(synth.GenKey(0, "tn", b, rnd, attempt),
+                         (cfg.N + 1, TV), std=2.0)
+    out = noise.astype(np.float64)
+    if d2t is None:
+        out += base
+    else:
+        out[:, d2t] += base
+    out = out.astype(np.float32)
+    out[tree["n_nodes"] + 1:] = 0.0
+    return out
+
+
+class ChainSeq:
+    """One sequence's oracle state across chained rounds."""
+
+    def __init__(self, model, seq, T, mode="keep", d2t=None, target_vocab=None,
+                 boost=0.0):
+        self.m, self.cfg, self.b = model, model.cfg, seq.b
+        self.kv, self.tree, self.info = seq.kv, seq.tree, seq.info
+        self.T, self.mode, self.d2t, self.TV = T, mode, d2t, target_vocab
+        self.boost = boost
+        self.len_out = seq.ctx + 1
+
+    def verify(self, rnd):
+        """Target logits for this round (noise redrawn while a sampling
+        decision sits within 1e-6 of its threshold) and the oracle's verify
+        and commit.  Returns (logits, result, new_len, seed rows, tokens)."""
+        for att in range(30):
+            tl = target_logits_for(self.m, self.tree, self.info, self.kv,
+                                   self.b, rnd, att, self.d2t, self.TV)
+            if self.boost:
+                # the target leans towards each row's best-valued child, so
+                # that paths get accepted and every commit case is reached
+                t = self.tree
+                for v in range(t["n_nodes"] + 1):
+                    if t["n_child"][v] > 0:
+                        kids = range(t["first_child"][v],
+                                     t["first_child"][v] + t["n_child"][v])
+                        best = max(kids, key=lambda c: t["score"][c])
+                        tl[v, t["token"][best]] += np.float32(self.boost)
+            res = O.verify(self.cfg, self.tree, tl, self.T, seed=SEED, rnd=rnd,
+                           b=self.b)
+            if self.T == 0 or res["margin"] >= 1e-6:
+                break
+        self.kv_before_commit = self.kv.copy()
+        new_len, rows, toks = O.commit(self.cfg, self.tree, res, self.kv,
+                                       mode=self.mode)
+        self.new_len, self.seed_rows, self.seed_toks = new_len, rows, toks
+        return tl, res
+
+    def draft(self, rnd):
+        """Fuse the next seed's synthetic target taps and draft the next tree
+        (taps redrawn while the tree's decision margin is below 1e-3)."""
+        cfg = self.cfg
+        for att in range(50):
+            feats = [synth.seed_features(cfg, self.b, rnd, r, att)
+                     for r in self.seed_rows]
+            taps = [np.stack([as_np(stored(cfg, f[i])) for f in feats])
+                    for i in range(3)]
+            g = O.fuse(self.m.oracle, *taps)
+            kv = self.kv.copy()
+            tree, info = O.draft_tree(self.m.oracle, kv, g, self.seed_toks,
+                                      self.new_len, d2t=self.d2t)
+            if O.decision_margin(cfg, info) >= MARGIN:
+                break
+        else:
+            raise RuntimeError("no input draw met the decision margin")
+        self.kv, self.tree, self.info, self.g = kv, tree, info, g
+        self.taps = taps
+        self.len_out = self.new_len + len(self.seed_rows)
+        return att

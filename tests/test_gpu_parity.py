@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import synth
-from harness import (MARGIN, Model, as_np, assert_tree_equal, cap_for,
+from harness import (MARGIN, SEED, Model, as_np, assert_tree_equal, cap_for,
                      gpu_tree_round, make_seq, stored, target_logits, tdtype,
                      tol, tree_to_np, upload_batch)
 
@@ -176,36 +176,52 @@ def test_verify_greedy_parity_with_commit(name):
 
 @pytest.mark.parametrize("name,T", [("tiny", 1.0), ("tiny", 0.6), ("mid", 1.0)])
 def test_verify_sampling_parity(name, T):
+    """Seeded rejection sampling: the library's Philox draws of (seed, round,
+    sequence) against the oracle's own Philox, over several rounds."""
     m, seqs, d, kv, tree = _run_tree_case(name, check_kv=False)
     cfg = m.cfg
     hits = 0
     for rnd in range(6):
         tl = []
-        us = []
         for s in seqs:
             for att in range(20):
                 t = target_logits(m, s, rnd, att)
                 # sharpen towards the drafter so children get accepted
                 t = (t * np.float32(3.0)).astype(np.float32)
-                u = synth.uniforms(cfg, s.b, rnd, cfg.N + 1, att)
-                w = O.verify(cfg, s.tree, t, T, u)
+                w = O.verify(cfg, s.tree, t, T, seed=SEED, rnd=rnd, b=s.b)
                 if w["margin"] >= 1e-6:
                     break
             tl.append(t)
-            us.append(u)
         tl = np.stack(tl)
-        us = np.stack(us).astype(np.float32)
-        res = d.verify(tree, torch.from_numpy(tl).cuda(), T,
-                       torch.from_numpy(us).cuda())
+        res = d.verify(tree, torch.from_numpy(tl).cuda(), T, seed=SEED, round=rnd)
         torch.cuda.synchronize()
         for b, s in enumerate(seqs):
-            want = O.verify(cfg, s.tree, tl[b], T, us[b])
+            want = O.verify(cfg, s.tree, tl[b], T, seed=SEED, rnd=rnd, b=b)
             hits += want["accept_len"]
             assert int(res["accept_len"][b]) == want["accept_len"]
             assert np.array_equal(res["tokens"][b].cpu().numpy(), want["tokens"])
             assert np.array_equal(res["accepted_rows"][b].cpu().numpy(),
                                   want["accepted_rows"])
     print(f"[verify] {name} T={T} accepted tokens over rounds: {hits}")
+
+
+def test_verify_explicit_uniforms_hook():
+    """The replay entry point with caller-drawn uniforms follows the same
+    Algorithm 1 walk as the oracle fed the same numbers."""
+    m, seqs, d, kv, tree = _run_tree_case("tiny", check_kv=False)
+    cfg = m.cfg
+    for rnd in range(4):
+        for att in range(20):
+            t = (target_logits(m, seqs[0], rnd, att) * np.float32(3.0)).astype(np.float32)
+            u = synth.uniforms(cfg, 0, rnd, cfg.N + 1, att)
+            w = O.verify(cfg, seqs[0].tree, t, 1.0, u)
+            if w["margin"] >= 1e-6:
+                break
+        res = d.verify(tree, torch.from_numpy(t[None]).cuda(), 1.0,
+                       uniforms=torch.from_numpy(u[None]).cuda())
+        torch.cuda.synchronize()
+        assert int(res["accept_len"][0]) == w["accept_len"]
+        assert np.array_equal(res["tokens"][0].cpu().numpy(), w["tokens"])
 
 
 def test_device_status_capacity():

@@ -14,7 +14,8 @@ STATUS_NAMES = {0: "ok", 1: "invalid argument", 2: "unsupported shape",
 EXPORTS = ("eagle_workspace_bytes", "eagle_create", "eagle_destroy",
            "eagle_status_str", "eagle_get_device_status", "eagle_fuse_features",
            "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree",
-           "eagle_verify_tree_uniforms", "eagle_draw_uniforms",
+           "eagle_verify_tree_uniforms", "eagle_verify_tree_noalloc",
+           "eagle_draw_uniforms",
            "eagle_profile", "eagle_profile_read")
 COMMIT_KEEP, COMMIT_RESEED = 0, 1
 STREAM_VERIFY, STREAM_DRAFT = 0, 1
@@ -102,6 +103,11 @@ def lib():
     L.eagle_verify_tree_uniforms.argtypes = [
         vp, ctypes.c_int32, ctypes.POINTER(Tree), vp, ctypes.c_float, vp,
         ctypes.c_int32, ctypes.POINTER(KV), vp, vp, vp, vp, vp, vp, vp]
+    L.eagle_verify_tree_noalloc.restype = ctypes.c_int
+    L.eagle_verify_tree_noalloc.argtypes = [
+        ctypes.POINTER(Config), ctypes.c_int32, ctypes.POINTER(Tree), vp,
+        ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32,
+        ctypes.POINTER(KV), vp, vp, vp, vp, vp, vp, vp]
     L.eagle_draw_uniforms.restype = ctypes.c_int
     L.eagle_draw_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
                                       ctypes.c_uint64, ctypes.c_int32,

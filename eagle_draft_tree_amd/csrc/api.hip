@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "../../include/eagle.h"
@@ -608,15 +609,23 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_sr
 
 namespace {
 
-eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
-                         const float* target_logits, float temperature,
-                         const float* uniforms, uint64_t seed, uint64_t round,
-                         int32_t commit_mode, const eagle_kv* kv_or_null,
+// Row statistics of a verification: where they live.
+struct VerifyScratch {
+  float* row_max;
+  double* row_sum;
+  int32_t* row_arg;
+  int32_t* row_bad;
+  int* status;
+};
+
+eagle_status verify_core(const eagle_config& cf, const VerifyScratch& ws, eagle_ctx* prof,
+                         int32_t batch, const eagle_tree* tree, const float* target_logits,
+                         float temperature, const float* uniforms, uint64_t seed,
+                         uint64_t round, int32_t commit_mode, const eagle_kv* kv_or_null,
                          int32_t* accept_len, int32_t* accepted_rows, int32_t* out_tokens,
                          int32_t* next_seed_rows, int32_t* next_seed_tokens,
                          int32_t* next_seed_len, hipStream_t stream) {
-  if (ctx == nullptr || null_tree(tree)) return EAGLE_EINVAL;
-  const eagle_config& cf = ctx->cfg;
+  if (null_tree(tree)) return EAGLE_EINVAL;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
   if (!(temperature >= 0.f) || !std::isfinite(temperature)) return EAGLE_EINVAL;
   if (!target_logits || !accept_len || !accepted_rows || !out_tokens ||
@@ -631,7 +640,6 @@ eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
   if (kv_or_null && (!kv_or_null->k || !kv_or_null->v || !kv_or_null->len_out ||
                      kv_or_null->cap < 1))
     return EAGLE_EINVAL;
-  const Offsets& f = ctx->off;
   VerifyParams p;
   p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = tvocab(cf);
   p.T = temperature; p.logits = target_logits; p.uniforms = uniforms;
@@ -639,8 +647,8 @@ eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
   p.t_token = tree->token; p.t_parent = tree->parent; p.t_depth = tree->depth;
   p.t_pos = tree->position; p.t_slot = tree->kv_slot; p.t_first = tree->first_child;
   p.t_nchild = tree->n_child; p.t_n = tree->n_nodes;
-  p.row_max = ctx->at<float>(f.v_max); p.row_sum = ctx->at<double>(f.v_sum);
-  p.row_arg = ctx->at<int32_t>(f.v_arg); p.row_bad = ctx->at<int32_t>(f.v_bad);
+  p.row_max = ws.row_max; p.row_sum = ws.row_sum;
+  p.row_arg = ws.row_arg; p.row_bad = ws.row_bad;
   p.accept_len = accept_len; p.accepted_rows = accepted_rows; p.out_tokens = out_tokens;
   p.seed_rows = next_seed_rows; p.seed_tokens = next_seed_tokens;
   p.seed_len = next_seed_len;
@@ -649,12 +657,76 @@ eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
   p.cap = kv_or_null ? kv_or_null->cap : 0;
   p.kv_len = kv_or_null ? kv_or_null->len_out : nullptr;
   p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.elem_bytes = esize(cf);
-  p.status = ctx->status();
-  const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * p.V * 4.0;
-  const int pi = prof_begin(ctx, PC_VERIFY, vbytes, 0.0, stream);
+  p.status = ws.status;
+  int pi = -1;
+  if (prof != nullptr) {
+    const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * p.V * 4.0;
+    pi = prof_begin(prof, PC_VERIFY, vbytes, 0.0, stream);
+  }
   const hipError_t e = launch_verify(p, stream);
-  prof_end(ctx, pi, stream);
+  if (prof != nullptr) prof_end(prof, pi, stream);
   return e == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+}
+
+eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                         const float* target_logits, float temperature,
+                         const float* uniforms, uint64_t seed, uint64_t round,
+                         int32_t commit_mode, const eagle_kv* kv_or_null,
+                         int32_t* accept_len, int32_t* accepted_rows, int32_t* out_tokens,
+                         int32_t* next_seed_rows, int32_t* next_seed_tokens,
+                         int32_t* next_seed_len, hipStream_t stream) {
+  if (ctx == nullptr) return EAGLE_EINVAL;
+  const Offsets& f = ctx->off;
+  VerifyScratch ws;
+  ws.row_max = ctx->at<float>(f.v_max);
+  ws.row_sum = ctx->at<double>(f.v_sum);
+  ws.row_arg = ctx->at<int32_t>(f.v_arg);
+  ws.row_bad = ctx->at<int32_t>(f.v_bad);
+  ws.status = ctx->status();
+  return verify_core(ctx->cfg, ws, ctx, batch, tree, target_logits, temperature, uniforms,
+                     seed, round, commit_mode, kv_or_null, accept_len, accepted_rows,
+                     out_tokens, next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Verification without a context or workspace: the row statistics live in a
+// fixed static device array, one copy per GPU, whose address is looked up
+// once per device and kept.
+// ---------------------------------------------------------------------------
+constexpr int kNoAllocRows = 16384;   // batch * (budget + 1) at most
+constexpr size_t kNaSum = 0;                                   // double [rows]
+constexpr size_t kNaMax = kNaSum + 8 * kNoAllocRows;           // float  [rows]
+constexpr size_t kNaArg = kNaMax + 4 * kNoAllocRows;           // int    [rows]
+constexpr size_t kNaBad = kNaArg + 4 * kNoAllocRows;           // int    [rows]
+constexpr size_t kNaStatus = kNaBad + 4 * kNoAllocRows;        // int
+constexpr size_t kNoAllocBytes = kNaStatus + 256;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// the row statistics of eagle_verify_tree_noalloc (one copy per GPU)
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's copy of `scratch`.  Host code must never pass
+// the array's own name to a kernel: on the host it only stands in for it.
+eagle_status scratch_on_current_device(unsigned char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EAGLE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return EAGLE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return EAGLE_EHIP;
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return EAGLE_OK;
 }
 
 }  // namespace
@@ -684,6 +756,35 @@ eagle_status eagle_verify_tree_uniforms(eagle_ctx* ctx, int32_t batch, const eag
   return verify_impl(ctx, batch, tree, target_logits, temperature, uniforms, 0, 0,
                      commit_mode, kv_or_null, accept_len, accepted_rows, out_tokens,
                      next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+eagle_status eagle_verify_tree_noalloc(const eagle_config* cfg, int32_t batch,
+                                       const eagle_tree* tree, const float* target_logits,
+                                       float temperature, uint64_t seed, uint64_t round,
+                                       int32_t commit_mode, const eagle_kv* kv_or_null,
+                                       int32_t* accept_len, int32_t* accepted_rows,
+                                       int32_t* out_tokens, int32_t* next_seed_rows,
+                                       int32_t* next_seed_tokens, int32_t* next_seed_len,
+                                       hipStream_t stream) {
+  const eagle_status st = check_config(cfg);
+  if (st != EAGLE_OK) return st;
+  if (batch < 1 || batch > cfg->max_batch) return EAGLE_EINVAL;
+  if (static_cast<int64_t>(batch) * (cfg->budget + 1) > kNoAllocRows)
+    return EAGLE_EUNSUPPORTED;
+  unsigned char* base = nullptr;
+  const eagle_status sp = scratch_on_current_device(&base);
+  if (sp != EAGLE_OK) return sp;
+  VerifyScratch ws;
+  ws.row_sum = reinterpret_cast<double*>(base + kNaSum);
+  ws.row_max = reinterpret_cast<float*>(base + kNaMax);
+  ws.row_arg = reinterpret_cast<int32_t*>(base + kNaArg);
+  ws.row_bad = reinterpret_cast<int32_t*>(base + kNaBad);
+  ws.status = reinterpret_cast<int*>(base + kNaStatus);
+  // the status word collects error bits with atomics: start it from zero
+  if (launch_fill_i32(ws.status, 0, 1, stream) != hipSuccess) return EAGLE_EHIP;
+  return verify_core(*cfg, ws, nullptr, batch, tree, target_logits, temperature, nullptr,
+                     seed, round, commit_mode, kv_or_null, accept_len, accepted_rows,
+                     out_tokens, next_seed_rows, next_seed_tokens, next_seed_len, stream);
 }
 
 eagle_status eagle_draw_uniforms(uint64_t seed, uint64_t stream_id, uint64_t round,

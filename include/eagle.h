@@ -270,6 +270,23 @@ eagle_status eagle_verify_tree_uniforms(
     int32_t *accepted_rows, int32_t *out_tokens, int32_t *next_seed_rows,
     int32_t *next_seed_tokens, int32_t *next_seed_len, hipStream_t stream);
 
+/* eagle_verify_tree for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no context and no workspace.  The same verification and
+ * commit, with the row statistics in a static device buffer of this library
+ * (about 320 KB per GPU, held until the process ends).  Limits: batch *
+ * (budget + 1) <= 16384, else EUNSUPPORTED; cfg is validated as by
+ * eagle_create.  Calls that overlap on one GPU share that buffer and race;
+ * order them.  Device-detected errors show only as accept_len = -1 (there is
+ * no status word to read).  Allocates nothing. */
+eagle_status eagle_verify_tree_noalloc(
+    const eagle_config *cfg, int32_t batch, const eagle_tree *tree,
+    const float *target_logits, float temperature, uint64_t seed,
+    uint64_t round, int32_t commit_mode, const eagle_kv *kv_or_null,
+    int32_t *accept_len, int32_t *accepted_rows, int32_t *out_tokens,
+    int32_t *next_seed_rows, int32_t *next_seed_tokens, int32_t *next_seed_len,
+    hipStream_t stream);
+
 /* The draws the sampling steps use ([E1] Algorithm 1: "draw r ~ U(0,1)"):
  * out[b, r, j] = U(seed, stream_id; counter (j, r, b, round)) for b < batch,
  * r < rows, j < draws, as described at eagle_verify_tree.  out is fp32

@@ -30,16 +30,44 @@ struct Layout {
 };
 
 struct Offsets {
-  size_t x, h, a0, a1, q, o, t, rn1, rn2, rnf, ss, part, cnt, lm_val, lm_id,
+  size_t x, h, a0, a1, q, o, t, ss, part, lm_val, lm_id,
       lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
       c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
       len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
-      cnt_gemm, cnt_done, cnt_attn;
-  int R, Rpad, nmax_part, ncnt, ntile_lm, qg, ncand;
+      cnt_attn, pack[7];
+  int R, Rpad, ncnt, ntile_lm, qg, ncand;
+  int64_t part_elems;
   size_t total;
 };
 
 int esize(const eagle_config& c) { return c.dtype == EAGLE_BF16 ? 2 : 4; }
+
+// The seven weight matrices the GEMMs stream, each packed once into the
+// workspace at create time.
+enum GemmId { G_FUSE = 0, G_IN, G_QKV, G_O, G_GU, G_DOWN, G_LM, G_COUNT };
+
+// N, K, sources and column map of GEMM `id` (sources only when w != null)
+void gemm_shape(const eagle_config& c, const eagle_weights* w, int id, GemmParams& p) {
+  const int H = c.hidden, F = c.ffn, V = c.vocab;
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  p.colmap = MAP_IDENT;
+  switch (id) {
+    case G_FUSE: p.N = H; p.K = 3 * H; if (w) p.w0 = w->w_fuse; break;
+    case G_IN: p.N = H; p.K = 2 * H; if (w) p.w0 = w->w_in; break;
+    case G_QKV:
+      p.N = qd + 2 * kd; p.K = H; p.colmap = MAP_QKV; p.qkv_n0 = qd; p.qkv_n1 = kd;
+      p.hd = c.head_dim;
+      if (w) { p.w0 = w->wq; p.w1 = w->wk; p.w2 = w->wv; }
+      break;
+    case G_O: p.N = H; p.K = qd; if (w) p.w0 = w->wo; break;
+    case G_GU:
+      p.N = 2 * F; p.K = H; p.colmap = MAP_SWIGLU;
+      if (w) { p.w0 = w->w_gate; p.w1 = w->w_up; }
+      break;
+    case G_DOWN: p.N = H; p.K = F; if (w) p.w0 = w->w_down; break;
+    default: p.N = V; p.K = H; if (w) p.w0 = w->w_lm; break;
+  }
+}
 // token ids of the tree, the embedding and the target logits
 int tvocab(const eagle_config& c) { return c.target_vocab > 0 ? c.target_vocab : c.vocab; }
 
@@ -86,12 +114,11 @@ Offsets make_layout(const eagle_config& c) {
   f.q = L.take(R * qd * es);
   f.o = L.take(R * qd * 4);
   f.t = L.take(R * F * 4);
-  f.rn1 = L.take(R * 4);
-  f.rn2 = L.take(R * 4);
-  f.rnf = L.take(R * 4);
   f.ss = L.take(R * (H / 16) * 4);
-  f.nmax_part = std::max(H, qd + 2 * kd);
-  f.part = L.take(8 * R * f.nmax_part * 4);
+  // split-K partials: up to 16 splits of 32 rows of the widest GEMM
+  const int maxN = std::max(std::max(V, 2 * F), std::max(3 * H, qd + 2 * kd));
+  f.part_elems = static_cast<int64_t>(16) * std::min<int64_t>(R, 32) * maxN;
+  f.part = L.take(static_cast<size_t>(f.part_elems) * 4);
   f.ntile_lm = (V + 63) / 64;
   f.lm_val = L.take(R * f.ntile_lm * c.topk * 4);
   f.lm_id = L.take(R * f.ntile_lm * c.topk * 4);
@@ -124,14 +151,15 @@ Offsets make_layout(const eagle_config& c) {
   f.v_arg = L.take(BN * 4);
   f.v_bad = L.take(BN * 4);
   // counters: zeroed once, every user resets what it touches
-  const int maxN = std::max(std::max(V, 2 * F), std::max(3 * H, qd + 2 * kd));
-  const size_t chunks = f.Rpad / 64;
   f.counters_begin = L.total;
-  f.cnt_gemm = L.take(chunks * (maxN / 16 + 1) * 4);
-  f.cnt_done = L.take(chunks * 4);
   f.cnt_attn = L.take(static_cast<size_t>(B) * c.n_kv_heads * 4);
   f.status = L.take(4);
   f.counters_end = L.total;
+  for (int id = 0; id < G_COUNT; ++id) {
+    GemmParams p;
+    gemm_shape(c, nullptr, id, p);
+    f.pack[id] = L.take(static_cast<size_t>(packed_elems(p.N, p.K)) * es);
+  }
   f.ncnt = static_cast<int>((f.counters_end - f.counters_begin) / 4);
   f.total = L.total;
   return f;
@@ -160,10 +188,13 @@ struct eagle_ctx {
   int num_cus;
   Profiler prof;
   template <typename P> P* at(size_t o) const { return reinterpret_cast<P*>(ws + o); }
-  int* cnt() const { return at<int>(off.cnt_gemm); }
-  int* done() const { return at<int>(off.cnt_done); }
   int* attn_cnt() const { return at<int>(off.cnt_attn); }
   int* status() const { return at<int>(off.status); }
+  // shape, column map and packed weights of GEMM `id`
+  void shape(int id, GemmParams& p) const {
+    gemm_shape(cfg, nullptr, id, p);
+    p.wpack = at<char>(off.pack[id]);
+  }
 };
 
 namespace {
@@ -206,19 +237,14 @@ struct Rows {  // one pass's query rows
 
 template <typename T>
 hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEMM) {
-  p.a_lo = 0;
   double a_bytes = 0;
-  for (int i = 0; i < p.nseg; ++i) {
-    if (sizeof(T) == 2) p.a_lo |= p.seg[i].f32;
+  for (int i = 0; i < p.nseg; ++i)
     a_bytes += static_cast<double>(p.M) * p.seg[i].width * (p.seg[i].f32 ? 4 : sizeof(T));
-  }
-  p.Mtot = c->off.Rpad;
+  p.Mtot = (p.M + 15) / 16 * 16;
   p.part = c->at<float>(c->off.part);
-  p.part_cols = 8 * c->off.nmax_part;
-  p.cnt = c->cnt();
-  p.done = c->done();
+  p.part_elems = c->off.part_elems;
   p.eps = c->cfg.rms_eps;
-  plan_gemm(p, c->num_cus);
+  plan_gemm(p, c->num_cus, sizeof(T) == 4);
   // algorithmic bytes: weights once, activation rows in, results out
   const double w_bytes = static_cast<double>(p.N) * p.K * sizeof(T);
   const double out_bytes = p.epi == EPI_LMHEAD ? 0.0 : static_cast<double>(p.M) * p.N * 4;
@@ -234,8 +260,8 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
                        hipStream_t s) {
   const eagle_config& cf = c->cfg;
   const Offsets& f = c->off;
-  const int H = cf.hidden, F = cf.ffn, V = cf.vocab;
-  const int qd = cf.n_q_heads * cf.head_dim, kd = cf.n_kv_heads * cf.head_dim;
+  const int H = cf.hidden, F = cf.ffn;
+  const int qd = cf.n_q_heads * cf.head_dim;
   const int R = r.batch * r.rps;
   hipError_t e;
 #define EAGLE_TRY(x)                 \
@@ -247,24 +273,24 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
   // a2 join: x = W_I [src ; E[tok]]
   {
     GemmParams p;
-    p.M = R; p.N = H; p.K = 2 * H; p.nseg = 2;
+    c->shape(G_IN, p);
+    p.M = R; p.nseg = 2;
     p.seg[0].base = r.src; p.seg[0].ld = H; p.seg[0].rowidx = r.src_row;
     p.seg[0].rowlimit = r.src_rows; p.seg[0].width = H;
     p.seg[1].base = c->w.embed; p.seg[1].ld = H; p.seg[1].rowidx = r.tok;
     p.seg[1].rowlimit = tvocab(cf); p.seg[1].width = H; p.seg[1].f32 = 0;
-    p.w0 = c->w.w_in;
     p.epi = EPI_STORE; p.out = c->at<char>(f.x); p.ldo = H;
-    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rn1);
+    p.ss = c->at<float>(f.ss);
     EAGLE_TRY(run_gemm<T>(c, p, s));
   }
   // a3 RMSNorm -> QKV -> RoPE -> q buffer + KV cache rows
   {
     GemmParams p;
-    p.M = R; p.N = qd + 2 * kd; p.K = H; p.nseg = 1;
+    c->shape(G_QKV, p);
+    p.M = R; p.nseg = 1;
     p.seg[0].base = c->at<char>(f.x); p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].rnorm = c->at<float>(f.rn1); p.seg[0].gain = c->w.g_attn;
-    p.w0 = c->w.wq; p.w1 = c->w.wk; p.w2 = c->w.wv;
-    p.colmap = MAP_QKV; p.qkv_n0 = qd; p.qkv_n1 = kd; p.hd = cf.head_dim;
+    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].gain = c->w.g_attn;
     p.epi = EPI_QKV; p.out = c->at<char>(f.q); p.ldo = qd;
     p.pos = r.pos; p.dest = r.dest; p.tok = r.tok; p.rows_per_seq = r.rps;
     p.kc = kv->k; p.vc = kv->v; p.cap = kv->cap; p.nq = cf.n_q_heads;
@@ -295,42 +321,44 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
   // a5 h = x + Wo o
   {
     GemmParams p;
-    p.M = R; p.N = H; p.K = qd; p.nseg = 1;
+    c->shape(G_O, p);
+    p.M = R; p.nseg = 1;
     p.seg[0].base = c->at<char>(f.o); p.seg[0].ld = qd; p.seg[0].width = qd;
-    p.w0 = c->w.wo;
     p.epi = EPI_RESID; p.out = c->at<char>(f.h); p.ldo = H;
     p.resid = c->at<float>(f.x); p.ldr = H;
-    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rn2);
+    p.ss = c->at<float>(f.ss);
     EAGLE_TRY(run_gemm<T>(c, p, s));
   }
   // a6 t = silu(Wg n2) * (Wu n2)
   {
     GemmParams p;
-    p.M = R; p.N = 2 * F; p.K = H; p.nseg = 1;
+    c->shape(G_GU, p);
+    p.M = R; p.nseg = 1;
     p.seg[0].base = c->at<char>(f.h); p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].rnorm = c->at<float>(f.rn2); p.seg[0].gain = c->w.g_mlp;
-    p.w0 = c->w.w_gate; p.w1 = c->w.w_up; p.colmap = MAP_SWIGLU;
+    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].gain = c->w.g_mlp;
     p.epi = EPI_SWIGLU; p.out = c->at<char>(f.t); p.ldo = F;
     EAGLE_TRY(run_gemm<T>(c, p, s));
   }
   //    a = h + Wd t
   {
     GemmParams p;
-    p.M = R; p.N = H; p.K = F; p.nseg = 1;
+    c->shape(G_DOWN, p);
+    p.M = R; p.nseg = 1;
     p.seg[0].base = c->at<char>(f.t); p.seg[0].ld = F; p.seg[0].width = F;
-    p.w0 = c->w.w_down;
     p.epi = EPI_RESID; p.out = r.a_out; p.ldo = H;
     p.resid = c->at<float>(f.h); p.ldr = H;
-    p.ss = c->at<float>(f.ss); p.rnorm_out = c->at<float>(f.rnf);
+    p.ss = c->at<float>(f.ss);
     EAGLE_TRY(run_gemm<T>(c, p, s));
   }
   // a7 final norm -> LM head -> per-tile top-k -> merge
   {
     GemmParams p;
-    p.M = R; p.N = V; p.K = H; p.nseg = 1;
+    c->shape(G_LM, p);
+    p.M = R; p.nseg = 1;
     p.seg[0].base = r.a_out; p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].rnorm = c->at<float>(f.rnf); p.seg[0].gain = c->w.g_final;
-    p.w0 = c->w.w_lm;
+    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].gain = c->w.g_final;
     p.epi = EPI_LMHEAD;
     p.cand_val = c->at<float>(f.lm_val); p.cand_id = c->at<int32_t>(f.lm_id);
     p.stat = c->at<float>(f.lm_stat); p.ntile_lm = f.ntile_lm; p.topk = cf.topk;
@@ -495,6 +523,17 @@ eagle_status eagle_create(const eagle_config* cfg, const eagle_weights* w,
     delete c;
     return EAGLE_EHIP;
   }
+  for (int id = 0; id < G_COUNT; ++id) {
+    GemmParams p;
+    gemm_shape(*cfg, w, id, p);
+    const hipError_t e = cfg->dtype == EAGLE_BF16
+                             ? launch_pack<uint16_t>(p, c->at<char>(off.pack[id]), stream)
+                             : launch_pack<float>(p, c->at<char>(off.pack[id]), stream);
+    if (e != hipSuccess) {
+      delete c;
+      return EAGLE_EHIP;
+    }
+  }
   *out = c;
   return EAGLE_OK;
 }
@@ -544,7 +583,8 @@ eagle_status eagle_fuse_features(eagle_ctx* ctx, int32_t rows, const void* low,
   for (int r0 = 0; r0 < rows; r0 += step) {
     const int m = std::min(step, rows - r0);
     GemmParams p;
-    p.M = m; p.N = H; p.K = 3 * H; p.nseg = 3;
+    ctx->shape(G_FUSE, p);
+    p.M = m; p.nseg = 3;
     const void* src[3] = {low, mid, high};
     for (int i = 0; i < 3; ++i) {
       p.seg[i].base = static_cast<const char*>(src[i]) + static_cast<size_t>(r0) * H * es;
@@ -552,7 +592,6 @@ eagle_status eagle_fuse_features(eagle_ctx* ctx, int32_t rows, const void* low,
       p.seg[i].width = H;
       p.seg[i].f32 = 0;
     }
-    p.w0 = ctx->w.w_fuse;
     p.epi = EPI_STORE;
     p.out = static_cast<float*>(g_out) + static_cast<size_t>(r0) * H;
     p.ldo = H;

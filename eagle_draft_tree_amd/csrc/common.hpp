@@ -53,6 +53,11 @@ template <> struct Frag8<uint16_t> {
   __device__ __forceinline__ void load(const uint16_t* p) {
     v = *reinterpret_cast<const u32x4*>(p);
   }
+  // streamed once: non-temporal loads keep HBM reads off the cache paths
+  // that cap ordinary loads at well under half the bandwidth
+  __device__ __forceinline__ void load_nt(const uint16_t* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = v[i >> 1];
     return bf2f(static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xffffu)));
@@ -77,6 +82,10 @@ template <> struct Frag8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   __device__ __forceinline__ float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
   __device__ __forceinline__ void set(int i, float x) {

@@ -1,18 +1,31 @@
-// Skinny MFMA GEMM for the draft path: C[M, N] = A[M, K] * W[N, K]^T with
-// M <= 64 rows per grid.z chunk (bs1 trees: M = 1..16).  At these shapes the
-// op is a weight stream from HBM, so the kernel is organised around the
-// weight reads:
-//  * each wave owns 16 output columns; every lane reads 64 contiguous bytes
-//    of one weight row per 128-wide k step (4 x 16-byte loads), and the k
-//    order inside a step is permuted identically for A and W so each 16x16x32
-//    MFMA consumes exactly what the lane loaded;
-//  * the next step's loads are issued before the current step's MFMAs;
-//  * waves of a workgroup split K (WK) or N (WN), and S workgroups split K
-//    further; partial sums go to a workspace and the last-arriving workgroup
-//    of a column group sums them in a fixed order (deterministic) and runs the
-//    fused epilogue;
-//  * the RMSNorm of the A operand is applied on load (factor per row computed
-//    by the producing GEMM's last workgroup), so no separate norm kernel runs.
+// Streaming MFMA GEMM for the draft path: C[M, N] = A[M, K] * W[N, K]^T with
+// M <= 64 rows per chunk (bs1 trees: M = 1..16).  At these shapes the op is
+// a stream of the weights from HBM, so the kernel is organised around them:
+//  * a workgroup owns 64 CT output columns (four waves of CT 16-column tiles)
+//    and one slice of K (S slices split K across workgroups);
+//  * its slice of A is normalised (RMSNorm factor and gain), split into
+//    bf16 hi + lo parts and laid out in LDS in MFMA fragment order once, at
+//    the start -- every wave then reads its A fragments with one 16-byte LDS
+//    load per MFMA;
+//  * the weights are packed once (pack_weights) in MFMA fragment order: for
+//    each 128-wide k step, 16-column tile and 32-wide sub-step e, the 64
+//    lanes' 8-element fragments lie contiguously, so every weight load of a
+//    wave reads 1 KB of contiguous memory (row-major tiles touch 16 rows per
+//    load and stream at well under half the bandwidth).  Tiles are
+//    interleaved per k step, so the waves that run together read neighbouring
+//    blocks and spread over all HBM channels instead of queuing on a few.  Lane (g, c) of
+//    sub-step e holds column c at k = step*128 + g*32 + e*8 .. +7; A is laid
+//    out with the same k permutation, so each 16x16x32 MFMA sums the right
+//    products.  kPF steps of loads stay in flight, with no branch in the
+//    loop body: steps past the slice re-read valid weights against an
+//    all-zero A block;
+//  * with one K split the epilogue is fused; with S splits the partial sums
+//    go to a workspace and a second kernel sums them in split order
+//    (deterministic) and runs the epilogue.  No workgroup waits on another:
+//    a device-scope fence here writes back the whole L2 of its XCD and costs
+//    far more than the launch;
+//  * RMSNorm of the A operand: the producer leaves per-16-column sums of
+//    squares, and each consumer workgroup derives the row factor itself.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,52 +33,11 @@ namespace eagle {
 
 namespace {
 
-constexpr int kStep = 128;  // k elements per wave step (4 lane groups x 32)
-
-struct ARow {
-  const void* ptr[3];
-  float r[3];
-};
-
-// A fragment for k in [k, k+8): float activation segments are normalised on
-// load (RMSNorm factor r and gain) and split for bf16 weights; weight-type
-// segments (embedding rows, target taps) load as they are.
-template <typename TW>
-__device__ __forceinline__ void load_a(const GemmParams& p, const ARow& ar,
-                                       int k, AFrag<TW>& f) {
-  int s = 0, base = 0;
-  if (p.nseg > 1 && k >= p.seg[0].width) {
-    base = p.seg[0].width;
-    s = 1;
-    if (p.nseg > 2 && k >= base + p.seg[1].width) {
-      base += p.seg[1].width;
-      s = 2;
-    }
-  }
-  const ASeg& sg = s == 0 ? p.seg[0] : (s == 1 ? p.seg[1] : p.seg[2]);
-  const void* rp = s == 0 ? ar.ptr[0] : (s == 1 ? ar.ptr[1] : ar.ptr[2]);
-  if (rp == nullptr) {
-    f.zero();
-    return;
-  }
-  const int kk = k - base;
-  if (sg.f32) {
-    Frag8<float> x;
-    x.load(static_cast<const float*>(rp) + kk);
-    if (sg.rnorm != nullptr) {
-      Frag8<TW> gf;
-      gf.load(static_cast<const TW*>(sg.gain) + kk);
-      const float r = s == 0 ? ar.r[0] : (s == 1 ? ar.r[1] : ar.r[2]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x.set(i, x.get(i) * r * gf.get(i));
-    }
-    f.from_float(x);
-  } else {
-    Frag8<TW> w;
-    w.load(static_cast<const TW*>(rp) + kk);
-    f.from_raw(w);
-  }
-}
+constexpr int kStep = 128;     // k elements per wave step (4 lane groups x 32)
+constexpr int kPF = 4;         // weight steps in flight per wave
+constexpr int kBlk = 2048;     // bytes of one (step, e, row tile) A block in LDS
+constexpr int kLdsCap = 130 * 1024;  // dynamic LDS a launch may use
+constexpr int kPackBlk = 512;  // elements of one packed (tile, step, e) block
 
 // global output column and weight row of tile column c
 __device__ __forceinline__ int tile_col(const GemmParams& p, int tile, int c) {
@@ -80,212 +52,185 @@ __device__ __forceinline__ int tile_col(const GemmParams& p, int tile, int c) {
 }
 
 template <typename T>
-__device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile,
-                                               int c) {
+__device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile, int c) {
   const int col = tile_col(p, tile, c);
   const int64_t K = p.K;
   if (p.colmap == MAP_QKV) {
     if (col < p.qkv_n0) return static_cast<const T*>(p.w0) + col * K;
-    if (col < p.qkv_n0 + p.qkv_n1)
-      return static_cast<const T*>(p.w1) + (col - p.qkv_n0) * K;
+    if (col < p.qkv_n0 + p.qkv_n1) return static_cast<const T*>(p.w1) + (col - p.qkv_n0) * K;
     return static_cast<const T*>(p.w2) + (col - p.qkv_n0 - p.qkv_n1) * K;
   }
-  if (p.colmap == MAP_SWIGLU)
-    return static_cast<const T*>(c < 8 ? p.w0 : p.w1) + col * K;
+  if (p.colmap == MAP_SWIGLU) return static_cast<const T*>(c < 8 ? p.w0 : p.w1) + col * K;
   return static_cast<const T*>(p.w0) + col * K;
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
 
+// 8 consecutive A elements of segment-local column kk of one row, as floats
+template <typename T>
+__device__ __forceinline__ void load8(const ASeg& sg, int64_t row, int kk, float (&v)[8]) {
+  if (sg.f32) {
+    const float* src = static_cast<const float*>(sg.base) + row * sg.ld + kk;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  } else {
+    Frag8<T> w;
+    w.load(static_cast<const T*>(sg.base) + row * sg.ld + kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = w.get(i);
+  }
+}
+
+// RMSNorm factors of rows m0 .. m0 + 16 MT of segment 0 (the only one that
+// may be normalised) from the producer's per-16-column sums of squares:
+// 1 / sqrt(mean(y^2) + eps), one value per row into rn.
+template <int MT>
+__device__ __forceinline__ void row_factors(const GemmParams& p, float* rn, int m0) {
+  const ASeg& sg = p.seg[0];
+  if (!sg.f32 || sg.ss == nullptr) return;
+  constexpr int TPR = 256 / (16 * MT);  // threads per row: 16, 8, 4
+  const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  const int row = m0 + r;
+  float q = 0.f;
+  if (row < p.M)
+    for (int t = part; t < sg.ss_tiles; t += TPR) q += sg.ss[static_cast<int64_t>(row) * sg.ss_tiles + t];
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) q += shfl_xor(q, o);
+  if (part == 0) rn[r] = 1.f / sqrtf(q / static_cast<float>(sg.width) + p.eps);
+}
+
+// Stage rows [m0, m0 + 16 MT) x k in [k0, kend) of A in LDS, fragment order:
+// block ((s * 4 + e) * MT + mt) holds, for each lane (g, c), the 8 values of
+// row mt*16 + c at k = k0 + s*128 + g*32 + e*8.  bf16: hi at lane*16 and lo
+// at 1024 + lane*16; fp32: values at lane*32.  The block after the last
+// (index nsteps * 4 * MT) is all zero.
+template <typename T, int MT>
+__device__ __forceinline__ void fill_a(const GemmParams& p, unsigned char* lds, const float* rn,
+                                       int m0, int k0, int kend, int nsteps) {
+  const int k8n = nsteps * 16;
+  const int total = MT * 16 * k8n;
+  for (int idx = threadIdx.x; idx < total; idx += 256) {
+    const int m = idx / k8n, k8 = idx - m * k8n;
+    const int k = k0 + 8 * k8;
+    const int row = m0 + m;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    if (row < p.M && k < kend) {
+      int si = 0, base = 0;
+      if (p.nseg > 1 && k >= p.seg[0].width) {
+        base = p.seg[0].width;
+        si = 1;
+        if (p.nseg > 2 && k >= base + p.seg[1].width) {
+          base += p.seg[1].width;
+          si = 2;
+        }
+      }
+      const ASeg& sg = si == 0 ? p.seg[0] : (si == 1 ? p.seg[1] : p.seg[2]);
+      int r = row;
+      if (sg.rowidx != nullptr) {
+        r = sg.rowidx[row];
+        if (r < 0 || r >= sg.rowlimit) r = -1;
+      }
+      if (r >= 0) {
+        const int kk = k - base;
+        load8<T>(sg, r, kk, v);
+        if (sg.f32 && sg.ss != nullptr) {
+          const float f = rn[m];
+          Frag8<T> gv;
+          gv.load(static_cast<const T*>(sg.gain) + kk);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
+        }
+      }
+    }
+    const int s = k8 >> 4, rem = k8 & 15;
+    const int g = rem >> 2, e = rem & 3;
+    const int mt = m >> 4, c = m & 15;
+    const int lane = g * 16 + c;
+    unsigned char* blk = lds + static_cast<size_t>((s * 4 + e) * MT + mt) * kBlk;
+    if constexpr (sizeof(T) == 2) {
+      Frag8<uint16_t> hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hi.set_pair(j, v[2 * j], v[2 * j + 1]);
+        lo.set_pair(j, v[2 * j] - hi.get(2 * j), v[2 * j + 1] - hi.get(2 * j + 1));
+      }
+      *reinterpret_cast<u32x4*>(blk + lane * 16) = hi.v;
+      *reinterpret_cast<u32x4*>(blk + 1024 + lane * 16) = lo.v;
+    } else {
+      *reinterpret_cast<f32x4*>(blk + lane * 32) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(blk + lane * 32 + 16) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+  }
+  // the zero block read by padding steps
+  unsigned char* zb = lds + static_cast<size_t>(nsteps * 4 * MT) * kBlk;
+  for (int i = threadIdx.x; i < kBlk / 16; i += 256)
+    *reinterpret_cast<u32x4*>(zb + i * 16) = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
 
-template <typename T, int MT>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmParams p) {
-  __shared__ float red[4 * 4 * 64 * 4];   // WK partial tiles / LM-head tile
-  __shared__ int flag;
-
+// Fused epilogue on the accumulators of one workgroup tile (column group
+// `group`, rows m0 .. m0 + 16 MT), lane layout of the 16x16 MFMA: lane
+// (g, c) of tile (mt, ct) holds rows mt*16 + 4g + j, column c.
+template <typename T, int MT, int CT>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][CT],
+                                         unsigned char* lds, int group, int m0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wn = wave % p.WN, wk = wave / p.WN;
   const int ntiles = p.N / 16;
-  const int ngroups = (ntiles + p.WN - 1) / p.WN;
-  const int group = blockIdx.x / p.S;
-  const int split = blockIdx.x % p.S;
-  const int tile = group * p.WN + wn;
-  const bool active = tile < ntiles;
-  const int m0 = blockIdx.z * 64;
-
-  // ---- per-lane A rows and W row -------------------------------------------
-  ARow ar[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m0 + mt * 16 + c;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      ar[mt].ptr[s] = nullptr;
-      ar[mt].r[s] = 1.f;
-      if (s < p.nseg && m < p.M) {
-        const ASeg& sg = p.seg[s];
-        int row = m;
-        if (sg.rowidx != nullptr) {
-          row = sg.rowidx[m];
-          if (row < 0 || row >= sg.rowlimit) row = -1;
-        }
-        if (row >= 0) {
-          const int64_t off = static_cast<int64_t>(row) * sg.ld;
-          ar[mt].ptr[s] = sg.f32 ? static_cast<const void*>(static_cast<const float*>(sg.base) + off)
-                                 : static_cast<const void*>(static_cast<const T*>(sg.base) + off);
-          if (sg.rnorm != nullptr) ar[mt].r[s] = sg.rnorm[m];
-        }
-      }
-    }
-  }
-  const T* wrow = active ? weight_row<T>(p, tile, c) : nullptr;
-
-  // ---- K loop ----------------------------------------------------------------
-  const int steps = (p.K + kStep - 1) / kStep;
-  const int nworkers = p.S * p.WK;
-  const int worker = split * p.WK + wk;
-  const int st0 = static_cast<int>((static_cast<int64_t>(worker) * steps) / nworkers);
-  const int st1 = static_cast<int>((static_cast<int64_t>(worker + 1) * steps) / nworkers);
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // weights are double-buffered (the HBM stream); activation fragments come
-  // from L2 and are loaded per step
-  Frag8<T> wa[4], wb[4];
-  auto load_w = [&](int st, Frag8<T>(&wf)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = st * kStep + g * 32 + e * 8;
-      if (active && k < p.K) wf[e].load(wrow + k); else wf[e].zero();
-    }
-  };
-  auto step = [&](int st, const Frag8<T>(&wf)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = st * kStep + g * 32 + e * 8;
-      const bool ok = active && k < p.K;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        AFrag<T> af;
-        if (ok) load_a<T>(p, ar[mt], k, af); else af.zero();
-        acc[mt] = mfma16(af.hi, wf[e], acc[mt]);
-        if constexpr (sizeof(T) == 2) {
-          if (p.a_lo) acc[mt] = mfma16(af.lo, wf[e], acc[mt]);
-        }
-      }
-    }
-  };
-
-  if (st0 < st1) load_w(st0, wa);
-  for (int st = st0; st < st1; st += 2) {
-    if (st + 1 < st1) load_w(st + 1, wb);
-    step(st, wa);
-    if (st + 2 < st1) load_w(st + 2, wa);
-    if (st + 1 < st1) step(st + 1, wb);
-  }
-
-  // ---- reduce the WK waves of this workgroup ---------------------------------
-  if (p.WK > 1) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        red[(((wk * p.WN + wn) * MT + mt) * 64 + lane) * 4 + j] = acc[mt][j];
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float s = 0.f;
-          for (int w = 0; w < p.WK; ++w)
-            s += red[(((w * p.WN + wn) * MT + mt) * 64 + lane) * 4 + j];
-          acc[mt][j] = s;
-        }
-    }
-    __syncthreads();
-  }
-
-  // ---- split-K across workgroups: last arrival finishes -----------------------
-  if (p.S > 1) {
-    if (wk == 0 && active) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + mt * 16 + 4 * g + j;
-          if (m < p.M)
-            p.part[(static_cast<int64_t>(split) * p.Mtot + m) * p.N + tile * 16 + c] =
-                acc[mt][j];
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int* ctr = p.cnt + blockIdx.z * ngroups + group;
-      const int prev = atomicAdd(ctr, 1);
-      flag = (prev == p.S - 1);
-      if (flag) atomicExch(ctr, 0);
-    }
-    __syncthreads();
-    if (!flag) return;
-    __threadfence();
-    if (wk == 0 && active) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + mt * 16 + 4 * g + j;
-          float s = 0.f;
-          if (m < p.M) {
-            for (int sp = 0; sp < p.S; ++sp)
-              s += __builtin_nontemporal_load(
-                  p.part + (static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c);
-          }
-          acc[mt][j] = s;
-        }
-    }
-  }
-
-  // ---- epilogues ---------------------------------------------------------------
+  // ---- epilogues -------------------------------------------------------------
   if (p.epi == EPI_LMHEAD) {
-    // WN == 4, WK == 1: the workgroup holds 64 consecutive vocabulary columns
-    float* lm = red;  // [64 rows][64 cols]
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        lm[(mt * 16 + 4 * g + j) * 64 + wn * 16 + c] = acc[mt][j];
+    // the workgroup holds 64 CT consecutive vocabulary columns; stage them in
+    // LDS and emit, per row and per 64-column tile, the top-k candidates and
+    // (max, sum of exp)
     __syncthreads();
-    const int rows = min(64, p.M - m0);
-    const int col = group * 64 + lane;
+    float* lm = reinterpret_cast<float*>(lds);  // [16 MT rows][64 CT cols]
+    constexpr int W = 64 * CT;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lm[(mt * 16 + 4 * g + j) * W + (wave * CT + ct) * 16 + c] = acc[mt][ct][j];
+    __syncthreads();
+    const int rows = min(16 * MT, p.M - m0);
     for (int r = wave; r < rows; r += 4) {
-      float v = col < p.N ? lm[r * 64 + lane] : -INFINITY;
-      if (v != v) v = -INFINITY;
-      int id = col < p.N ? col : 0x7fffffff;
-      const float mx = wave_max(v);
-      const float se = wave_sum(v == -INFINITY ? 0.f : expf(v - mx));
-      wave_sort_desc(v, id);
-      const int m = m0 + r;
-      const int64_t o = static_cast<int64_t>(m) * p.ntile_lm + group;
-      if (lane < p.topk) {
-        p.cand_val[o * p.topk + lane] = v;
-        p.cand_id[o * p.topk + lane] = id;
-      }
-      if (lane == 0) {
-        p.stat[o * 2] = mx;
-        p.stat[o * 2 + 1] = se;
+#pragma unroll
+      for (int ch = 0; ch < CT; ++ch) {
+        const int lt = group * CT + ch;   // 64-column LM tile
+        if (lt >= p.ntile_lm) continue;
+        const int col = lt * 64 + lane;
+        float v = col < p.N ? lm[r * W + ch * 64 + lane] : -INFINITY;
+        if (v != v) v = -INFINITY;
+        int id = col < p.N ? col : 0x7fffffff;
+        const float mx = wave_max(v);
+        const float se = wave_sum(v == -INFINITY ? 0.f : expf(v - mx));
+        wave_sort_desc(v, id);
+        const int m = m0 + r;
+        const int64_t o = static_cast<int64_t>(m) * p.ntile_lm + lt;
+        if (lane < p.topk) {
+          p.cand_val[o * p.topk + lane] = v;
+          p.cand_id[o * p.topk + lane] = id;
+        }
+        if (lane == 0) {
+          p.stat[o * 2] = mx;
+          p.stat[o * 2 + 1] = se;
+        }
       }
     }
     return;
   }
 
-  if (wk == 0 && active) {
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+    if (tile >= ntiles) continue;
     if (p.epi == EPI_STORE || p.epi == EPI_RESID) {
       float* out = static_cast<float*>(p.out);
       const int col = tile * 16 + c;
@@ -294,7 +239,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int m = m0 + mt * 16 + 4 * g + j;
-          float y = acc[mt][j];
+          float y = acc[mt][ct][j];
           if (m < p.M && p.epi == EPI_RESID) y += p.resid[m * p.ldr + col];
           if (m < p.M) out[m * p.ldo + col] = y;
           if (p.ss != nullptr) {
@@ -314,9 +259,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int m = m0 + mt * 16 + 4 * g + j;
-          const float other = shfl_xor(acc[mt][j], 8);
-          if (c < 8 && m < p.M)
-            out[m * p.ldo + f] = silu(acc[mt][j]) * other;
+          const float other = shfl_xor(acc[mt][ct][j], 8);
+          if (c < 8 && m < p.M) out[m * p.ldo + f] = silu(acc[mt][ct][j]) * other;
         }
     } else if (p.epi == EPI_QKV) {
       const int col = tile_col(p, tile, c);
@@ -331,7 +275,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int m = m0 + mt * 16 + 4 * g + j;
-          const float x = acc[mt][j];
+          const float x = acc[mt][ct][j];
           const float other = shfl_xor(x, 8);
           if (m >= p.M || p.tok[m] < 0) continue;
           float y = x;
@@ -360,66 +304,285 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmParams p) {
     }
   }
 
-  // ---- last finishing group of the chunk computes the RMSNorm factors ------
-  if (p.ss != nullptr && p.rnorm_out != nullptr) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(p.done + blockIdx.z, 1);
-      flag = (prev == ngroups - 1);
-      if (flag) atomicExch(p.done + blockIdx.z, 0);
-    }
-    __syncthreads();
-    if (!flag) return;
-    __threadfence();
-    const int rows = min(64, p.M - m0);
-    for (int r = wave; r < rows; r += 4) {
-      const int m = m0 + r;
-      float s = 0.f;
-      for (int t = lane; t < ntiles; t += 64)
-        s += __builtin_nontemporal_load(p.ss + m * ntiles + t);
-      s = wave_sum(s);
-      if (lane == 0) p.rnorm_out[m] = 1.f / sqrtf(s / static_cast<float>(p.N) + p.eps);
-    }
-  }
 }
 
-void plan_gemm(GemmParams& p, int num_cus) {
+template <typename T, int MT, int CT, int PS>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
+  // weight steps in flight per wave; a piece of PS steps is fully unrolled,
+  // so buffer (s % PF) always holds step s of the piece
+  constexpr int PF = PS < kPF ? PS : kPF;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
   const int ntiles = p.N / 16;
-  const int chunks = (p.M + 63) / 64;
-  if (p.epi == EPI_LMHEAD) {
-    p.WN = 4;
-    p.WK = 1;
-    p.S = 1;
+  const int group = blockIdx.x / p.S;
+  const int split = blockIdx.x % p.S;
+  const int m0 = blockIdx.z * (16 * MT);
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int st0 = split * (p.KS / kStep);
+  const int nsteps = min(p.KS / kStep, ksteps - st0);
+  const int kend = min(p.K, st0 * kStep + p.KS);
+
+  // ---- per-lane weight fragments in the packed layout (inactive tiles read
+  // tile 0 and are dropped) ----
+  const T* wtile[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+    wtile[ct] = static_cast<const T*>(p.wpack) +
+                static_cast<int64_t>(tile < ntiles ? tile : 0) * 4 * kPackBlk + lane * 8;
+  }
+  // weight fragments of step st (clamped into the slice): one fully
+  // coalesced 1 KB (bf16) load per wave and fragment
+  const int64_t step_stride = static_cast<int64_t>(ntiles) * 4 * kPackBlk;
+  auto load_w = [&](int st, Frag8<T>(&wf)[CT][4]) {
+    const int sc = min(st, st0 + nsteps - 1);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wf[ct][e].load_nt(wtile[ct] + sc * step_stride + e * kPackBlk);
+  };
+
+  __shared__ float rn[16 * MT];
+  row_factors<MT>(p, rn, m0);
+  __syncthreads();
+
+  Frag8<T> wb[PF][CT][4];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load_w(st0 + i, wb[i]);
+  // the first PF steps of weights are in flight while A is staged
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4 acc[MT][CT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ps0 = 0; ps0 < nsteps; ps0 += PS) {
+    const int np = min(PS, nsteps - ps0);
+    if (ps0 > 0) __syncthreads();  // every wave is done with the last piece
+    fill_a<T, MT>(p, lds, rn, m0, (st0 + ps0) * kStep, kend, np);
+    __syncthreads();
+    const int zero_blk = np * 4 * MT;
+#pragma unroll
+    for (int s = 0; s < PS; ++s) {
+      const int i = s % PF;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int blk = s < np ? (s * 4 + e) * MT + mt : zero_blk;
+          const unsigned char* ap = lds + static_cast<size_t>(blk) * kBlk;
+          if constexpr (sizeof(T) == 2) {
+            Frag8<uint16_t> ah, al;
+            ah.v = *reinterpret_cast<const u32x4*>(ap + lane * 16);
+            al.v = *reinterpret_cast<const u32x4*>(ap + 1024 + lane * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              acc[mt][ct] = mfma16(ah, wb[i][ct][e], acc[mt][ct]);
+              acc[mt][ct] = mfma16(al, wb[i][ct][e], acc[mt][ct]);
+            }
+          } else {
+            Frag8<float> af;
+            af.a = *reinterpret_cast<const f32x4*>(ap + lane * 32);
+            af.b = *reinterpret_cast<const f32x4*>(ap + lane * 32 + 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              acc[mt][ct] = mfma16(af, wb[i][ct][e], acc[mt][ct]);
+          }
+        }
+      }
+      // refill this buffer right after its last use: keep the compiler from
+      // sinking the loads, which would shorten the stream in flight
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(st0 + ps0 + s + PF, wb[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- split-K: partial sums to the workspace, the epilogue kernel sums ---
+  if (p.S > 1) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int tile = (group * 4 + wave) * CT + ct;
+      if (tile >= ntiles) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = m0 + mt * 16 + 4 * g + j;
+          if (m < p.M)
+            p.part[(static_cast<int64_t>(split) * p.Mtot + m) * p.N + tile * 16 + c] =
+                acc[mt][ct][j];
+        }
+    }
     return;
   }
-  p.WN = 1;
-  p.WK = 4;
-  const int steps = (p.K + kStep - 1) / kStep;
-  const int want_waves = 16 * num_cus;
-  int S = want_waves / (ntiles * p.WK * chunks);
-  S = S < 1 ? 1 : (S > 8 ? 8 : S);
-  while (S > 1 && S * p.WK > steps) --S;
-  while (S > 1 && S * p.N > p.part_cols) --S;
-  if (p.WK > steps) p.WK = steps < 1 ? 1 : (steps >= 4 ? 4 : (steps >= 2 ? 2 : 1));
-  p.S = S;
+  epilogue<T, MT, CT>(p, acc, lds, group, m0);
+}
+
+// Split-K finish: sums the S partial tiles of a column group in split order
+// (deterministic) and runs the fused epilogue.  A kernel boundary, not a
+// fence, orders the partial sums of all workgroups before this kernel.
+template <typename T, int MT, int CT>
+__global__ __launch_bounds__(256) void epilogue_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int ntiles = p.N / 16;
+  const int group = blockIdx.x;
+  const int m0 = blockIdx.z * (16 * MT);
+  f32x4 acc[MT][CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + mt * 16 + 4 * g + j;
+        float sum = 0.f;
+        if (m < p.M && tile < ntiles) {
+          for (int sp = 0; sp < p.S; ++sp)
+            sum += p.part[(static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c];
+        }
+        acc[mt][ct][j] = sum;
+      }
+  }
+  epilogue<T, MT, CT>(p, acc, lds, group, m0);
 }
 
 template <typename T>
-hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+__global__ __launch_bounds__(256) void pack_weights_kernel(GemmParams p, T* dst) {
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int tile = blockIdx.x / ksteps, st = blockIdx.x % ksteps;
+  const int e = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int k = st * kStep + g * 32 + e * 8;
+  Frag8<T> v;
+  if (k < p.K) v.load(weight_row<T>(p, tile, c) + k); else v.zero();
   const int ntiles = p.N / 16;
-  const int ngroups = (ntiles + p.WN - 1) / p.WN;
-  const int chunks = (p.M + 63) / 64;
-  const int mt = chunks > 1 ? 4 : (p.M + 15) / 16;
-  dim3 grid(ngroups * p.S, 1, chunks);
-  dim3 block(256);
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((skinny_gemm_kernel<T, 1>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((skinny_gemm_kernel<T, 2>), grid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((skinny_gemm_kernel<T, 3>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((skinny_gemm_kernel<T, 4>), grid, block, 0, s, p); break;
+  T* out = dst + ((static_cast<int64_t>(st) * ntiles + tile) * 4 + e) * kPackBlk + lane * 8;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<u32x4*>(out) = v.v;
+  } else {
+    *reinterpret_cast<f32x4*>(out) = v.a;
+    *reinterpret_cast<f32x4*>(out + 4) = v.b;
   }
+}
+
+int64_t packed_elems(int N, int K) {
+  return static_cast<int64_t>(N) * ((K + kStep - 1) / kStep) * kStep;
+}
+
+template <typename T>
+hipError_t launch_pack(const GemmParams& p, void* dst, hipStream_t s) {
+  if (p.N % 16 || p.K % 8 || p.K < 8) return hipErrorInvalidValue;
+  const int64_t blocks = static_cast<int64_t>(p.N / 16) * ((p.K + kStep - 1) / kStep);
+  hipLaunchKernelGGL(pack_weights_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     p, static_cast<T*>(dst));
   return hipGetLastError();
+}
+template hipError_t launch_pack<uint16_t>(const GemmParams&, void*, hipStream_t);
+template hipError_t launch_pack<float>(const GemmParams&, void*, hipStream_t);
+
+namespace {
+
+size_t lds_bytes(int MT, int steps) { return static_cast<size_t>(steps * 4 * MT + 1) * kBlk; }
+// most k steps of A one LDS piece holds: 8 / 4 / 4 for 1 / 2 / 4 row tiles
+// (66 KB, 66 KB and 130 KB of LDS)
+int max_piece(int MT) { return MT == 1 ? 8 : 4; }
+
+}  // namespace
+
+void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
+  const int ntiles = p.N / 16;
+  const int rows = p.M < 64 ? p.M : 64;
+  p.MT = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int chunks = (p.M + 16 * p.MT - 1) / (16 * p.MT);
+  // two 16-column tiles per wave for wide GEMMs (bf16 only: fp32 fragments
+  // take twice the registers)
+  p.CT = (!fp32 && ntiles >= 2 * num_cus) ? 2 : 1;
+  const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int pmax = max_piece(p.MT);
+  // a split stages at most one piece; more splits while the grid is short of
+  // two workgroups per CU and each split keeps at least two steps
+  int S = (ksteps + pmax - 1) / pmax;
+  const int want = 2 * num_cus;
+  while (ngroups * chunks * S < want && (ksteps + S) / (S + 1) >= 2) ++S;
+  // the partial sums must fit the workspace; a split may then span pieces
+  while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
+  const int steps = (ksteps + S - 1) / S;
+  p.KS = steps * kStep;
+  p.S = (ksteps + steps - 1) / steps;
+  // smallest unrolled piece that holds the slice (several pieces otherwise)
+  p.piece_steps = steps <= 2 ? 2 : (steps <= 4 ? 4 : pmax);
+}
+
+namespace {
+
+template <typename T, int MT, int CT, int PS>
+hipError_t launch_one(const GemmParams& p, hipStream_t s) {
+  const int ntiles = p.N / 16;
+  const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
+  const int chunks = (p.M + 16 * MT - 1) / (16 * MT);
+  size_t lds = lds_bytes(MT, PS);
+  const size_t tile_bytes = static_cast<size_t>(16 * MT) * 64 * CT * 4;
+  if (lds < tile_bytes) lds = tile_bytes;
+  if (lds > static_cast<size_t>(kLdsCap)) return hipErrorInvalidValue;
+  auto kern = stream_gemm_kernel<T, MT, CT, PS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsCap);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(ngroups * p.S, 1, chunks), dim3(256), lds, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S == 1) return e;
+  hipLaunchKernelGGL((epilogue_kernel<T, MT, CT>), dim3(ngroups, 1, chunks), dim3(256),
+                     tile_bytes, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int MT, int CT>
+hipError_t launch_ps(const GemmParams& p, hipStream_t s) {
+  switch (p.piece_steps) {
+    case 2: return launch_one<T, MT, CT, 2>(p, s);
+    case 4: return launch_one<T, MT, CT, 4>(p, s);
+    default:
+      if constexpr (MT == 1) return launch_one<T, MT, CT, 8>(p, s);
+      return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int MT>
+hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (p.CT == 2) return launch_ps<T, MT, 2>(p, s);
+  }
+  return launch_ps<T, MT, 1>(p, s);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  if (p.N % 16 || p.K % 8 || p.K < 8 || p.KS % kStep || p.S < 1 ||
+      static_cast<int64_t>(p.S) * p.KS < p.K || (p.S > 1 && p.part == nullptr) ||
+      (p.CT == 2 && sizeof(T) != 2) || p.wpack == nullptr)
+    return hipErrorInvalidValue;
+  // a split either fits one piece or spans whole pieces of 4 or 8 steps
+  if (p.KS / kStep > p.piece_steps && p.piece_steps < 4) return hipErrorInvalidValue;
+  switch (p.MT) {
+    case 1: return launch_mt<T, 1>(p, s);
+    case 2: return launch_mt<T, 2>(p, s);
+    default: return launch_mt<T, 4>(p, s);
+  }
 }
 
 template hipError_t launch_gemm<uint16_t>(const GemmParams&, hipStream_t);

@@ -22,7 +22,8 @@ struct ASeg {
   const int32_t* rowidx = nullptr;  // optional row gather; <0 or >= rowlimit -> zero row
   int rowlimit = 0;
   int width = 0;                  // K elements in this segment (multiple of 8)
-  const float* rnorm = nullptr;   // optional RMSNorm factor per A row
+  const float* ss = nullptr;      // optional RMSNorm: per-row sums of squares of
+  int ss_tiles = 0;               //   the producer, [rows, ss_tiles] partials
   const void* gain = nullptr;     // RMSNorm gain [width] (weight type)
   int f32 = 1;                    // elements are float activations (else weight type)
 };
@@ -31,27 +32,28 @@ struct GemmParams {
   int M = 0, N = 0, K = 0;        // N: logical output columns (multiple of 16)
   int nseg = 1;
   ASeg seg[3];
-  const void* w0 = nullptr;       // weights [rows, K]; see ColMap
+  const void* wpack = nullptr;    // weights packed by launch_pack (read by the GEMM)
+  const void* w0 = nullptr;       // weights [rows, K]; see ColMap (read by the packer)
   const void* w1 = nullptr;
   const void* w2 = nullptr;
   int colmap = MAP_IDENT;
   int qkv_n0 = 0, qkv_n1 = 0;     // columns served by w0, then w1, rest w2
   int hd = 0;
-  int S = 1, WN = 1, WK = 4;      // split-K over WGs, waves along N and K
-  int a_lo = 0;                   // bf16 weights with float A rows: add the lo MFMA
+  // launch plan (plan_gemm): row tiles MT x 16 rows per chunk, CT 16-column
+  // tiles per wave (a workgroup covers 64 CT columns), S splits of K of KS
+  // elements each (KS a multiple of 128)
+  int MT = 1, CT = 1, S = 1, KS = 128;
+  int piece_steps = 8;            // k steps of A staged in LDS at a time
   int Mtot = 0;                   // padded rows of the partial buffer
   float* part = nullptr;          // [S, Mtot, N] split-K partials
-  int part_cols = 0;              // S * N must not exceed this
-  int* cnt = nullptr;             // per (chunk, group) arrival counters
-  int* done = nullptr;            // per chunk finished-group counters
+  int64_t part_elems = 0;         // capacity of part (floats)
   int epi = EPI_STORE;
   void* out = nullptr;            // float activations (q: weight type)
   int64_t ldo = 0;
   const float* resid = nullptr;
   int64_t ldr = 0;
-  float* ss = nullptr;            // [M, N/16] partial sums of squares
-  float* rnorm_out = nullptr;     // [M] 1/sqrt(mean(y^2) + eps)
-  float eps = 1e-5f;
+  float* ss = nullptr;            // [M, N/16] sums of squares per 16-column tile
+  float eps = 1e-5f;              // RMSNorm epsilon of the A operand
   // QKV epilogue
   const int32_t* pos = nullptr;
   const int32_t* dest = nullptr;
@@ -69,7 +71,11 @@ struct GemmParams {
   int ntile_lm = 0, topk = 0;
 };
 
-void plan_gemm(GemmParams& p, int num_cus);
+void plan_gemm(GemmParams& p, int num_cus, bool fp32);
+// Weights of one GEMM (w0..w2, colmap, N, K of p) copied into dst in the
+// MFMA fragment order the GEMM streams; packed_elems(N, K) elements.
+int64_t packed_elems(int N, int K);
+template <typename T> hipError_t launch_pack(const GemmParams& p, void* dst, hipStream_t s);
 template <typename T> hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // tree attention --------------------------------------------------------------

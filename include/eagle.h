@@ -151,12 +151,15 @@ typedef struct eagle_ctx eagle_ctx;
  * config is invalid. */
 size_t eagle_workspace_bytes(const eagle_config *cfg);
 
-/* Validates cfg, records the weight pointers (not copied; they must outlive
- * the context) and takes `workspace` (device, >= eagle_workspace_bytes,
- * 256-byte aligned) for the context's lifetime.  Clears the workspace's
- * counters with a kernel on `stream`; with a d2t map it synchronises
- * `stream` and checks the map on the host.  *out receives a host-allocated
- * context.  Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
+/* Validates cfg, takes `workspace` (device, >= eagle_workspace_bytes,
+ * 256-byte aligned) for the context's lifetime and copies the seven GEMM
+ * weight matrices (w_fuse, w_in, wq/wk/wv, wo, w_gate/w_up, w_down, w_lm)
+ * into it in the tile order the kernels stream, with kernels on `stream`;
+ * later writes to those buffers are not seen.  embed, the gains and d2t are
+ * read in place and must outlive the context.  Clears the workspace's
+ * counters; with a d2t map it synchronises `stream` and checks the map on
+ * the host.  *out receives a host-allocated context.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
 eagle_status eagle_create(const eagle_config *cfg, const eagle_weights *w,
                           void *workspace, size_t ws_bytes, hipStream_t stream,
                           eagle_ctx **out);

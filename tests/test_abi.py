@@ -55,8 +55,9 @@ def test_workspace_bytes_and_config_validation():
                 dict(max_seed=16, n_q_heads=16, n_kv_heads=1)):
         assert L.eagle_workspace_bytes(ctypes.byref(_cfg(**bad))) == 0, bad
     # larger batch needs more workspace
+    small = L.eagle_workspace_bytes(ctypes.byref(_cfg(dtype=0, max_batch=1)))
     big = L.eagle_workspace_bytes(ctypes.byref(_cfg(dtype=0, max_batch=8)))
-    assert big > ok
+    assert big > small > 0
 
 
 def test_null_arguments_rejected_on_host():

@@ -77,13 +77,13 @@ class Workload:
         gen.manual_seed(seed)
         ctx = torch.from_numpy(synth.contexts(cfg)).to(torch.int32)
         self.ctx = ctx
-        cap = int(ctx.max()) + cfg.s_max + (cfg.D - 1) * cfg.K + 64
+        cap = (int(ctx.max()) + cfg.s_max + (cfg.D - 1) * cfg.K + 64 + 7) // 8 * 8
         k = torch.zeros(B, cfg.n_kv, cap, cfg.hd, dtype=dt, device="cuda")
-        v = torch.zeros_like(k)
+        v = torch.zeros(B, cfg.n_kv, cfg.hd, cap, dtype=dt, device="cuda")
         for b in range(B):
             L = int(ctx[b])
             k[b, :, :L] = torch.randn(cfg.n_kv, L, cfg.hd, generator=gen, device="cuda").to(dt)
-            v[b, :, :L] = torch.randn(cfg.n_kv, L, cfg.hd, generator=gen, device="cuda").to(dt)
+            v[b, :, :, :L] = torch.randn(cfg.n_kv, cfg.hd, L, generator=gen, device="cuda").to(dt)
         self.kv = KVCache(k, v, ctx.cuda())
         self.d = Drafter(DrafterShape(
             hidden=cfg.H, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv, head_dim=cfg.hd,

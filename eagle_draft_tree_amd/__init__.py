@@ -64,12 +64,25 @@ def _stream():
 
 
 class KVCache:
-    """Draft KV cache [B, n_kv, cap, hd] plus committed lengths [B] (int32)."""
+    """Draft KV cache: k [B, n_kv, cap, hd] (key rows), v [B, n_kv, hd, cap]
+    (values stored transposed), committed lengths [B] (int32); cap is a
+    multiple of 8."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, length: torch.Tensor):
-        assert k.shape == v.shape and k.dim() == 4 and k.is_contiguous()
+        assert k.dim() == 4 and v.dim() == 4 and k.is_contiguous() and v.is_contiguous()
+        assert k.shape[:2] == v.shape[:2] and k.shape[2] == v.shape[3] and \
+            k.shape[3] == v.shape[2], "v is [B, n_kv, hd, cap]"
         self.k, self.v = k, v
         self.length = length.to(torch.int32).contiguous()
+
+    @classmethod
+    def from_rows(cls, k: torch.Tensor, v_rows: torch.Tensor, length: torch.Tensor):
+        """From key and value rows, both [B, n_kv, cap, hd]."""
+        return cls(k.contiguous(), v_rows.transpose(-1, -2).contiguous(), length)
+
+    def v_rows(self) -> torch.Tensor:
+        """The values as rows, [B, n_kv, cap, hd] (a view)."""
+        return self.v.transpose(-1, -2)
 
     @property
     def cap(self) -> int:

@@ -17,7 +17,12 @@ using namespace eagle;
 
 namespace {
 
-constexpr int kMaxSplit = 32;
+// Most prefix splits of the tree attention for a batch: enough waves to fill
+// the chip at batch 1, a bounded partial-sum buffer at large batch.
+int attn_max_split(int batch, int nkv) {
+  const int w = 4096 / std::max(1, batch * nkv);
+  return std::min(64, std::max(4, w));
+}
 constexpr size_t kAlign = 256;
 
 struct Layout {
@@ -34,8 +39,8 @@ struct Offsets {
       lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
       c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
       len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
-      cnt_attn, pack[7];
-  int R, Rpad, ncnt, ntile_lm, qg, ncand;
+      cnt_gemm, pack[7];
+  int R, Rpad, ncnt, ntile_lm, qg, ncand, max_split;
   int64_t part_elems;
   size_t total;
 };
@@ -127,7 +132,8 @@ Offsets make_layout(const eagle_config& c) {
   f.tk_val = L.take(R * c.topk * 4);
   f.lse = L.take(R * 4);
   f.qg = rps * (c.n_q_heads / c.n_kv_heads);
-  const size_t bk = static_cast<size_t>(B) * c.n_kv_heads * (kMaxSplit + 1) * f.qg;
+  f.max_split = attn_max_split(B, c.n_kv_heads);
+  const size_t bk = static_cast<size_t>(B) * c.n_kv_heads * (f.max_split + 1) * f.qg;
   f.at_o = L.take(bk * c.head_dim * 4);
   f.at_ml = L.take(bk * 2 * 4);
   for (int s = 0; s < 2; ++s)
@@ -152,7 +158,7 @@ Offsets make_layout(const eagle_config& c) {
   f.v_bad = L.take(BN * 4);
   // counters: zeroed once, every user resets what it touches
   f.counters_begin = L.total;
-  f.cnt_attn = L.take(static_cast<size_t>(B) * c.n_kv_heads * 4);
+  f.cnt_gemm = L.take(static_cast<size_t>(f.Rpad / 16 + 1) * (maxN / 64 + 1) * 4);
   f.status = L.take(4);
   f.counters_end = L.total;
   for (int id = 0; id < G_COUNT; ++id) {
@@ -188,7 +194,6 @@ struct eagle_ctx {
   int num_cus;
   Profiler prof;
   template <typename P> P* at(size_t o) const { return reinterpret_cast<P*>(ws + o); }
-  int* attn_cnt() const { return at<int>(off.cnt_attn); }
   int* status() const { return at<int>(off.status); }
   // shape, column map and packed weights of GEMM `id`
   void shape(int id, GemmParams& p) const {
@@ -243,6 +248,7 @@ hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEM
   p.Mtot = (p.M + 15) / 16 * 16;
   p.part = c->at<float>(c->off.part);
   p.part_elems = c->off.part_elems;
+  p.cnt = c->at<int>(c->off.cnt_gemm);
   p.eps = c->cfg.rms_eps;
   plan_gemm(p, c->num_cus, sizeof(T) == 4);
   // algorithmic bytes: weights once, activation rows in, results out
@@ -306,13 +312,16 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     p.q = c->at<char>(f.q); p.o = c->at<float>(f.o);
     p.kc = kv->k; p.vc = kv->v; p.tok = r.tok; p.plen = r.plen;
     p.sbase = r.sbase; p.smask = r.mask;
-    int nsplit = std::min(kMaxSplit, std::max(1, (kv->cap + 63) / 64));
-    int chunk = (kv->cap + nsplit - 1) / nsplit;
-    chunk = std::max(64, (chunk + 63) / 64 * 64);
-    nsplit = std::max(1, (kv->cap + chunk - 1) / chunk);
-    p.nsplit = nsplit; p.chunk = chunk;
+    // splits: about 8192 waves over the batch (each keeps only one 32-key
+    // step of K and V in flight), at least 64 keys each
+    const int G = cf.n_q_heads / cf.n_kv_heads;
+    const int nqg = ((r.rps * G + 15) / 16 + 1) / 2;
+    const int want = std::max(1, 8192 / std::max(1, r.batch * cf.n_kv_heads * nqg));
+    int nsplit = std::min({f.max_split, std::max(1, (kv->cap + 63) / 64), want});
+    const int split_keys = std::max(64, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);
+    nsplit = (kv->cap + split_keys - 1) / split_keys;
+    p.nsplit = nsplit; p.split_keys = split_keys;
     p.part_o = c->at<float>(f.at_o); p.part_ml = c->at<float>(f.at_ml);
-    p.cnt = c->attn_cnt();
     p.scale = 1.0f / sqrtf(static_cast<float>(cf.head_dim));
     const int pi = prof_begin(c, PC_ATTN, 0.0, 0.0, s);
     EAGLE_TRY(launch_attention<T>(p, s));
@@ -615,7 +624,7 @@ eagle_status eagle_draft_step(eagle_ctx* ctx, int32_t batch, int32_t rows_per_se
       rows_per_seq > std::max(cf.max_seed, cf.topk))
     return EAGLE_EINVAL;
   if (!src || !token || !position || !dest || !prefix_len || !scratch_base ||
-      !scratch_mask || !kv->k || !kv->v || kv->cap < 1 || !a_out || !topk_id ||
+      !scratch_mask || !kv->k || !kv->v || kv->cap < 8 || kv->cap % 8 || !a_out || !topk_id ||
       !topk_logit || !lse)
     return EAGLE_EINVAL;
   Rows r;
@@ -635,7 +644,7 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_sr
   const eagle_config& cf = ctx->cfg;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
   if (!seed_src || !seed_token || !seed_len || !kv->k || !kv->v || !kv->len_in ||
-      !kv->len_out || kv->cap < 1)
+      !kv->len_out || kv->cap < 8 || kv->cap % 8)
     return EAGLE_EINVAL;
   return cf.dtype == EAGLE_BF16
              ? draft_tree_impl<uint16_t>(ctx, batch, seed_src, seed_token, seed_len, kv,
@@ -677,7 +686,7 @@ eagle_status verify_core(const eagle_config& cf, const VerifyScratch& ws, eagle_
   if (cf.max_seed < (commit_mode == EAGLE_COMMIT_RESEED ? cf.depth + 1 : 2))
     return EAGLE_EUNSUPPORTED;
   if (kv_or_null && (!kv_or_null->k || !kv_or_null->v || !kv_or_null->len_out ||
-                     kv_or_null->cap < 1))
+                     kv_or_null->cap < 8 || kv_or_null->cap % 8))
     return EAGLE_EINVAL;
   VerifyParams p;
   p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = tvocab(cf);

@@ -1,15 +1,24 @@
-// Tree attention of the draft layer.
+// Tree attention of the draft layer (split-KV, "flash decoding" style).
 //
-// One workgroup per (split, kv head, sequence).  The query vectors of a
-// sequence that share a kv head (rows_per_seq rows x G grouped heads, at most
-// 128) form the MFMA columns; 64-key tiles of K and V are staged in LDS
-// (V transposed) and shared by the four waves.  Scores are S^T = K Q^T, so
-// each lane ends up owning one query column, which is also the column layout
-// of O^T = V^T P^T: the online-softmax state never leaves the lane group.
-// Visibility per query row: cache rows [0, prefix_len) (prefix splits) and
-// the scratch rows scratch_base + j whose bit j is set in the row's 64-bit
-// ancestor mask (one extra split).  Partial (max, sum, O) per split go to the
-// workspace; the last split of a (sequence, kv head) to finish merges them.
+// The query vectors of a sequence that share a kv head (rows_per_seq rows x
+// G grouped heads, at most 128) are the MFMA columns.  Every wave owns one
+// key range (a split) and up to QBW blocks of 16 query vectors, and runs the
+// online softmax over its keys with the state in registers:
+//  * S^T = K Q^T: K rows are read straight from the cache as MFMA A
+//    fragments (lane (g, c): key c, 32 contiguous dims), Q as B fragments
+//    with the same dim permutation; lane (g, c) ends up holding keys
+//    4g + i of query column c;
+//  * O^T += V^T P^T: the V cache is stored transposed ([hd, cap] per head),
+//    so lane (g, c) reads its 8 keys of dim c as two 4-key runs -- exactly
+//    the keys whose probabilities it already holds, which makes them the B
+//    fragment with no data movement.  In bf16, P is carried as hi + lo bf16
+//    parts, so o keeps float precision;
+//  * visibility: cache rows [0, prefix_len) of the query's row (prefix
+//    splits) and scratch rows scratch_base + j for the set bits j of the
+//    row's 64-bit ancestor mask (the last split).
+// Keys are visited 32 at a time, which keeps a wave within 256 registers.
+// Each wave writes its (max, sum, O) per query vector; a second kernel
+// merges the splits in split order.  No workgroup waits on another.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,15 +26,13 @@ namespace eagle {
 
 namespace {
 
-template <typename T> struct Vec16;
-template <> struct Vec16<uint16_t> { static constexpr int n = 8; };
-template <> struct Vec16<float> { static constexpr int n = 4; };
+constexpr int QBW = 2;   // 16-query blocks per wave
 
+// 4 consecutive elements of T into half of a fragment
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, Frag8<T>& f, int half);
 template <>
-__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, Frag8<uint16_t>& f,
-                                                int half) {
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, Frag8<uint16_t>& f, int half) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
   f.v[2 * half] = v.x;
   f.v[2 * half + 1] = v.y;
@@ -39,156 +46,166 @@ __device__ __forceinline__ void load4<float>(const float* p, Frag8<float>& f, in
 }  // namespace
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
-  constexpr int KS = HD + 8;   // padded K row (elements)
-  constexpr int VS = 64 + 8;   // padded V^T row (elements)
-  constexpr int NE = HD / 32;  // frag8 per lane per query vector
-  constexpr int NHB = HD / 16; // 16-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
-  __shared__ int s_kmax;
-  __shared__ uint64_t s_umask;
-  __shared__ int s_last;
-
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
+  constexpr int NE = HD / 32;   // 8-element fragments per lane per query / key
+  constexpr int NB = HD / 16;   // 16-dim blocks of O^T
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
-  const int nmb = (QG + 15) / 16;
+  const int nqb = (QG + 15) / 16;
+  const int nqg = (nqb + QBW - 1) / QBW;
   const int NS = p.nsplit + 1;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= NS * nqg) return;
+  const int split = item / nqg, qgrp = item % nqg;
   const bool scratch = split == p.nsplit;
   const int row0 = b * p.rows_per_seq;
 
-  if (threadIdx.x == 0) {
-    int km = 0;
-    uint64_t um = 0;
-    for (int i = 0; i < p.rows_per_seq; ++i) {
-      if (p.tok[row0 + i] < 0) continue;
-      km = max(km, min(p.plen[row0 + i], p.cap));
-      um |= p.smask[row0 + i];
-    }
-    s_kmax = km;
-    s_umask = um;
+  // keys any row of this sequence may see: lane i reads row i, then a wave
+  // reduction (rows_per_seq <= 16)
+  int kmax = 0;
+  uint64_t umask = 0;
+  if (lane < p.rows_per_seq && p.tok[row0 + lane] >= 0) {
+    kmax = min(p.plen[row0 + lane], p.cap);
+    umask = p.smask[row0 + lane];
   }
-  __syncthreads();
-  const int kmax = s_kmax;
-  const uint64_t umask = s_umask;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    kmax = max(kmax, shfl_xor(kmax, o));
+    const uint32_t lo = static_cast<uint32_t>(umask), hi = static_cast<uint32_t>(umask >> 32);
+    const uint32_t olo = static_cast<uint32_t>(shfl_xor(static_cast<int>(lo), o));
+    const uint32_t ohi = static_cast<uint32_t>(shfl_xor(static_cast<int>(hi), o));
+    umask |= (static_cast<uint64_t>(ohi) << 32) | olo;
+  }
+  kmax = __shfl(kmax, 0, 64);
+  umask = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(umask >> 32), 0, 64))) << 32) |
+          static_cast<uint32_t>(__shfl(static_cast<int>(umask), 0, 64));
   const int sbase = p.sbase[b];
-
   int kbeg, kend;
   if (scratch) {
-    kbeg = 0;
-    kend = umask ? 64 : 0;
+    // the two 32-slot halves of the 64-bit ancestor mask
+    kbeg = (umask & 0xffffffffull) ? 0 : 32;
+    kend = umask ? ((umask >> 32) ? 64 : 32) : 0;
   } else {
-    kbeg = split * p.chunk;
-    kend = min(kbeg + p.chunk, kmax);
+    kbeg = split * p.split_keys;
+    kend = min(kbeg + p.split_keys, kmax);
   }
 
-  // per-wave query blocks (at most 2: QG <= 128)
-  Frag8<T> qf[2][NE];
-  f32x4 oacc[2][NHB];
-  float mrun[2], lrun[2];
-  int qrow[2], qhead[2];
-  bool qok[2];
-  int plen_c[2];
-  uint64_t mask_c[2];
+  // query fragments and per-column state
+  Frag8<T> qf[QBW][NE];
+  f32x4 oacc[QBW][NB];
+  float mrun[QBW], lrun[QBW];
+  bool qok[QBW];
+  int plen_c[QBW];
+  uint64_t mask_c[QBW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int mb = wave + 4 * u;
+  for (int u = 0; u < QBW; ++u) {
+    const int mb = qgrp * QBW + u;
     const int m = mb * 16 + c;
     const int i = m / G;
-    qok[u] = mb < nmb && m < QG && p.tok[row0 + min(i, p.rows_per_seq - 1)] >= 0;
-    qrow[u] = row0 + (qok[u] ? i : 0);
-    qhead[u] = kvh * G + m % G;
-    plen_c[u] = qok[u] ? min(p.plen[qrow[u]], p.cap) : 0;
-    mask_c[u] = qok[u] ? p.smask[qrow[u]] : 0ull;
+    const int row = row0 + min(i, p.rows_per_seq - 1);
+    qok[u] = mb < nqb && m < QG && p.tok[row] >= 0;
+    plen_c[u] = qok[u] ? min(p.plen[row], p.cap) : 0;
+    mask_c[u] = qok[u] ? p.smask[row] : 0ull;
     mrun[u] = -INFINITY;
     lrun[u] = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) oacc[u][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) oacc[u][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int head = kvh * G + m % G;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      if (qok[u]) {
-        const T* qp = static_cast<const T*>(p.q) +
-                      (static_cast<int64_t>(qrow[u]) * p.nq + qhead[u]) * HD +
-                      g * (HD / 4) + 8 * e;
-        qf[u][e].load(qp);
-      } else {
+      if (qok[u])
+        qf[u][e].load(static_cast<const T*>(p.q) + (static_cast<int64_t>(row) * p.nq + head) * HD +
+                      g * (HD / 4) + 8 * e);
+      else
         qf[u][e].zero();
-      }
     }
   }
 
-  const T* kc = static_cast<const T*>(p.kc) +
-                (static_cast<int64_t>(b) * p.nkv + kvh) * p.cap * HD;
-  const T* vc = static_cast<const T*>(p.vc) +
-                (static_cast<int64_t>(b) * p.nkv + kvh) * p.cap * HD;
-  constexpr int VN = Vec16<T>::n;
-  constexpr int CPR = HD / VN;  // 16-byte chunks per row
+  const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
+  const T* kc = static_cast<const T*>(p.kc) + bk * p.cap * HD;
+  const T* vt = static_cast<const T*>(p.vc) + bk * HD * p.cap;
 
-  for (int t0 = kbeg; t0 < kend; t0 += 64) {
-    // ---- stage K and V^T tiles ----
-    for (int ch = threadIdx.x; ch < 64 * CPR; ch += 256) {
-      const int key = ch / CPR, h = (ch % CPR) * VN;
-      const int ci = scratch ? sbase + key : t0 + key;
-      const bool ok = scratch ? (((umask >> key) & 1ull) && ci >= 0 && ci < p.cap)
-                              : (t0 + key < kend);
-      Frag8<T> kv;  // used as a 16-byte carrier
-      if constexpr (sizeof(T) == 2) {
-        u32x4 kk = u32x4{0u, 0u, 0u, 0u}, vv = kk;
-        if (ok) {
-          kk = *reinterpret_cast<const u32x4*>(kc + static_cast<int64_t>(ci) * HD + h);
-          vv = *reinterpret_cast<const u32x4*>(vc + static_cast<int64_t>(ci) * HD + h);
-        }
-        *reinterpret_cast<u32x4*>(&Ks[key * KS + h]) = kk;
+  // 32-key steps: K fragments (two 16-key blocks) and V^T fragments of the
+  // same keys, then the online-softmax update of every query block
+  for (int t0 = kbeg; t0 < kend; t0 += 32) {
+    // cache index of step key j (0..31) and whether any query may see it
+    auto key_index = [&](int j) { return scratch ? sbase + t0 + j : t0 + j; };
+    auto key_live = [&](int j) {
+      if (scratch) return ((umask >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
+      return t0 + j < kend;
+    };
+    // ---- K fragments (A operand): lane (g, c) = key kb*16 + c ----
+    Frag8<T> kf[2][NE];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Vt[(h + e) * VS + key] =
-              static_cast<T>((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
-      } else {
-        f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, vv = kk;
-        if (ok) {
-          kk = *reinterpret_cast<const f32x4*>(kc + static_cast<int64_t>(ci) * HD + h);
-          vv = *reinterpret_cast<const f32x4*>(vc + static_cast<int64_t>(ci) * HD + h);
-        }
-        *reinterpret_cast<f32x4*>(&Ks[key * KS + h]) = kk;
+    for (int kb = 0; kb < 2; ++kb) {
+      const int j = kb * 16 + c;
+      const int ci = key_live(j) ? key_index(j) : (scratch ? 0 : t0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Vt[(h + e) * VS + key] = vv[e];
-      }
-      (void)kv;
+      for (int e = 0; e < NE; ++e)
+        kf[kb][e].load_nt(kc + static_cast<int64_t>(ci) * HD + g * (HD / 4) + 8 * e);
     }
-    __syncthreads();
-
+    // ---- V^T fragments (A operand of O^T = V^T P^T): dim nb*16 + c, keys
+    // {4g + i} (elements 0..3) and {16 + 4g + i} (4..7); dead keys read as
+    // zero.  In a prefix step the four keys of a half are contiguous and
+    // 8-byte aligned (cap is a multiple of 8); scratch slots start at an
+    // arbitrary row and are read one by one ----
+    Frag8<T> vf[NB];
+    if (!scratch) {
+      // a prefix run of 4 keys starting below cap is readable (cap is a
+      // multiple of 8); keys past kend are zeroed after the load
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int mb = wave + 4 * u;
-      if (mb >= nmb) continue;
-      // S^T block: keys x query columns
-      f32x4 s[4];
+      for (int half = 0; half < 2; ++half) {
+        const int j0 = 16 * half + 4 * g;
+        const bool inb = t0 + j0 < p.cap;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) {
+          const int d = nb * 16 + c;
+          if (inb) load4<T>(vt + static_cast<int64_t>(d) * p.cap + t0 + j0, vf[nb], half);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          Frag8<T> kf;
-          kf.load(&Ks[(kb * 16 + c) * KS + g * (HD / 4) + 8 * e]);
-          s[kb] = mfma16(kf, qf[u][e], s[kb]);
+          for (int i = 0; i < 4; ++i)
+            if (!inb || !key_live(j0 + i)) vf[nb].set(4 * half + i, 0.f);
         }
       }
-      // mask + scale, tile max
+    } else {
+      // scratch slots start at an arbitrary row: element by element
+      for (int nb = 0; nb < NB; ++nb) {
+        const int d = nb * 16 + c;
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int j = 16 * (e8 >> 2) + 4 * g + (e8 & 3);
+          const float x = key_live(j)
+                              ? Elem<T>::to_f(vt[static_cast<int64_t>(d) * p.cap + key_index(j)])
+                              : 0.f;
+          vf[nb].set(e8, x);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int u = 0; u < QBW; ++u) {
+      if (qgrp * QBW + u >= nqb) continue;
+      // S^T block: 32 keys x 16 query columns
+      f32x4 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < NE; ++e) sc[kb] = mfma16(kf[kb][e], qf[u][e], sc[kb]);
+      }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kl = kb * 16 + 4 * g + j;
+        for (int i = 0; i < 4; ++i) {
+          const int j = kb * 16 + 4 * g + i;
           bool vis;
-          if (scratch) vis = ((mask_c[u] >> kl) & 1ull) != 0;
-          else vis = (t0 + kl) < plen_c[u] && (t0 + kl) < kend;
+          if (scratch) vis = ((mask_c[u] >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
+          else vis = t0 + j < plen_c[u] && t0 + j < kend;
           vis = vis && qok[u];
-          const float v = vis ? s[kb][j] * p.scale : -INFINITY;
-          s[kb][j] = v;
+          const float v = vis ? sc[kb][i] * p.scale : -INFINITY;
+          sc[kb][i] = v;
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
@@ -198,119 +215,114 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       if (mnew != -INFINITY) {
         alpha = (mrun[u] == -INFINITY) ? 0.f : expf(mrun[u] - mnew);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float pv = (s[kb][j] == -INFINITY) ? 0.f : expf(s[kb][j] - mnew);
-            s[kb][j] = pv;
+          for (int i = 0; i < 4; ++i) {
+            const float pv = (sc[kb][i] == -INFINITY) ? 0.f : expf(sc[kb][i] - mnew);
+            sc[kb][i] = pv;
             psum += pv;
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       psum += shfl_xor(psum, 16);
       psum += shfl_xor(psum, 32);
       lrun[u] = lrun[u] * alpha + psum;
       mrun[u] = mnew;
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) oacc[u][hb] *= alpha;
-      // O^T += V^T P^T over two 32-key halves
-      // In bf16, P is carried as hi + lo bf16 parts (2^-17 relative), so the
-      // only roundings of o are fp32 accumulation and its final storage.
+      for (int nb = 0; nb < NB; ++nb) oacc[u][nb] *= alpha;
+      // P^T fragment: the lane's own probabilities, keys {4g + i} (elements
+      // 0..3) and {16 + 4g + i} (elements 4..7)
+      Frag8<T> ph, pl;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        Frag8<T> pf, pl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = s[2 * h2][j], p1 = s[2 * h2 + 1][j];
-          pf.set(j, p0);
-          pf.set(4 + j, p1);
-          if constexpr (sizeof(T) == 2) {
-            pl.set(j, p0 - pf.get(j));
-            pl.set(4 + j, p1 - pf.get(4 + j));
-          }
-        }
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          Frag8<T> vf;
-          const T* vrow = &Vt[(hb * 16 + c) * VS];
-          load4<T>(vrow + (2 * h2) * 16 + 4 * g, vf, 0);
-          load4<T>(vrow + (2 * h2 + 1) * 16 + 4 * g, vf, 1);
-          oacc[u][hb] = mfma16(vf, pf, oacc[u][hb]);
-          if constexpr (sizeof(T) == 2) oacc[u][hb] = mfma16(vf, pl, oacc[u][hb]);
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = sc[0][i], p1 = sc[1][i];
+        ph.set(i, p0);
+        ph.set(4 + i, p1);
+        if constexpr (sizeof(T) == 2) {
+          pl.set(i, p0 - ph.get(i));
+          pl.set(4 + i, p1 - ph.get(4 + i));
         }
       }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        oacc[u][nb] = mfma16(vf[nb], ph, oacc[u][nb]);
+        if constexpr (sizeof(T) == 2) oacc[u][nb] = mfma16(vf[nb], pl, oacc[u][nb]);
+      }
     }
-    __syncthreads();
   }
 
-  // ---- write this split's partial ----
-  const int bk = b * p.nkv + kvh;
+  // ---- this split's partial (max, sum, O) per query vector ----
+  const int NSP = p.nsplit + 1;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int mb = wave + 4 * u;
+  for (int u = 0; u < QBW; ++u) {
+    const int mb = qgrp * QBW + u;
     const int m = mb * 16 + c;
-    if (mb >= nmb || m >= QG) continue;
-    const int64_t base = (static_cast<int64_t>(bk) * NS + split) * QG + m;
+    if (mb >= nqb || m >= QG) continue;
+    const int64_t base = (bk * NSP + split) * QG + m;
     if (g == 0) {
       p.part_ml[base * 2] = mrun[u];
       p.part_ml[base * 2 + 1] = lrun[u];
     }
-    if (mrun[u] != -INFINITY) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p.part_o[base * HD + hb * 16 + 4 * g + j] = oacc[u][hb][j];
-    }
+      for (int i = 0; i < 4; ++i) p.part_o[base * HD + nb * 16 + 4 * g + i] = oacc[u][nb][i];
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(p.cnt + bk, 1);
-    s_last = prev == NS - 1;
-    if (s_last) atomicExch(p.cnt + bk, 0);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // ---- merge all splits ----
-  for (int idx = threadIdx.x; idx < QG * HD; idx += 256) {
-    const int m = idx / HD, h = idx % HD;
-    const int i = m / G;
-    const int row = row0 + i;
-    if (p.tok[row] < 0) continue;
-    float M = -INFINITY;
-    for (int sp = 0; sp < NS; ++sp) {
-      const int64_t base = (static_cast<int64_t>(bk) * NS + sp) * QG + m;
-      M = fmaxf(M, __builtin_nontemporal_load(p.part_ml + base * 2));
-    }
+// Merge of the splits: one workgroup per (query vector, kv head, sequence),
+// one thread per dim; splits are combined in order (deterministic).
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
+  const int m = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = p.nq / p.nkv;
+  const int QG = p.rows_per_seq * G;
+  const int row = b * p.rows_per_seq + m / G;
+  if (m >= QG || p.tok[row] < 0) return;
+  const int NSP = p.nsplit + 1;
+  const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
+  float M = -INFINITY;
+  for (int sp = 0; sp < NSP; ++sp) M = fmaxf(M, p.part_ml[((bk * NSP + sp) * QG + m) * 2]);
+  const int head = kvh * G + m % G;
+  for (int d = threadIdx.x; d < p.hd; d += blockDim.x) {
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
-      for (int sp = 0; sp < NS; ++sp) {
-        const int64_t base = (static_cast<int64_t>(bk) * NS + sp) * QG + m;
-        const float ms = __builtin_nontemporal_load(p.part_ml + base * 2);
+      for (int sp = 0; sp < NSP; ++sp) {
+        const int64_t base = (bk * NSP + sp) * QG + m;
+        const float ms = p.part_ml[base * 2];
         if (ms == -INFINITY) continue;
         const float w = expf(ms - M);
-        L += w * __builtin_nontemporal_load(p.part_ml + base * 2 + 1);
-        O += w * __builtin_nontemporal_load(p.part_o + base * HD + h);
+        L += w * p.part_ml[base * 2 + 1];
+        O += w * p.part_o[base * p.hd + d];
       }
     }
-    const float y = L > 0.f ? O / L : 0.f;
-    const int head = kvh * G + m % G;
-    p.o[(static_cast<int64_t>(row) * p.nq + head) * HD + h] = y;
+    p.o[(static_cast<int64_t>(row) * p.nq + head) * p.hd + d] = L > 0.f ? O / L : 0.f;
   }
 }
 
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  dim3 grid(p.nsplit + 1, p.nkv, p.batch);
-  if (p.hd == 128)
-    hipLaunchKernelGGL((tree_attn_kernel<T, 128>), grid, dim3(256), 0, s, p);
-  else
+  const int G = p.nq / p.nkv;
+  const int QG = p.rows_per_seq * G;
+  if (QG > 128 || p.split_keys % 64 || p.split_keys < 64) return hipErrorInvalidValue;
+  const int nqb = (QG + 15) / 16;
+  const int nqg = (nqb + QBW - 1) / QBW;
+  const int items = (p.nsplit + 1) * nqg;
+  dim3 grid((items + 3) / 4, p.nkv, p.batch);
+  if constexpr (sizeof(T) == 2) {
+    if (p.hd == 128)
+      hipLaunchKernelGGL((tree_attn_kernel<T, 128>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((tree_attn_kernel<T, 64>), grid, dim3(256), 0, s, p);
+  } else {
+    // fp32 storage is supported with head_dim 64 only
+    if (p.hd != 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL((tree_attn_kernel<T, 64>), grid, dim3(256), 0, s, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(QG, p.nkv, p.batch), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

@@ -19,11 +19,9 @@
 //    products.  kPF steps of loads stay in flight, with no branch in the
 //    loop body: steps past the slice re-read valid weights against an
 //    all-zero A block;
-//  * with one K split the epilogue is fused; with S splits the partial sums
-//    go to a workspace and a second kernel sums them in split order
-//    (deterministic) and runs the epilogue.  No workgroup waits on another:
-//    a device-scope fence here writes back the whole L2 of its XCD and costs
-//    far more than the launch;
+//  * with S K-splits the partial sums go to a workspace and the last
+//    workgroup of a column group to arrive sums them in split order
+//    (deterministic) and runs the fused epilogue;
 //  * RMSNorm of the A operand: the producer leaves per-16-column sums of
 //    squares, and each consumer workgroup derives the row factor itself.
 #include "common.hpp"
@@ -297,8 +295,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
             }
             const bool isk = hh < p.nq + p.nkv;
             const int kvh = isk ? hh - p.nq : hh - p.nq - p.nkv;
-            T* cache = static_cast<T*>(isk ? p.kc : p.vc);
-            cache[((static_cast<int64_t>(b) * p.nkv + kvh) * p.cap + d) * p.hd + cin] = v;
+            const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
+            // K rows [cap, hd]; V stored transposed, [hd, cap]
+            if (isk) static_cast<T*>(p.kc)[(bk * p.cap + d) * p.hd + cin] = v;
+            else static_cast<T*>(p.vc)[(bk * p.hd + cin) * p.cap + d] = v;
           }
         }
     }
@@ -402,8 +402,15 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
     }
   }
 
-  // ---- split-K: partial sums to the workspace, the epilogue kernel sums ---
+  // ---- split-K: the last workgroup of a column group to arrive sums ------
+  // Partial tiles are written and read with agent-scope atomic (relaxed)
+  // stores and loads, which the memory model maps to accesses coherent at
+  // device scope (sc1: written through, read past the XCD's L2), and the
+  // stores have completed (vmcnt 0) before the arrival counter moves.  A
+  // device-scope release fence would do the same by writing back the whole
+  // L2 of the XCD, which costs more than the GEMM.
   if (p.S > 1) {
+    __shared__ int last;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int tile = (group * 4 + wave) * CT + ct;
@@ -414,42 +421,40 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
         for (int j = 0; j < 4; ++j) {
           const int m = m0 + mt * 16 + 4 * g + j;
           if (m < p.M)
-            p.part[(static_cast<int64_t>(split) * p.Mtot + m) * p.N + tile * 16 + c] =
-                acc[mt][ct][j];
+            __hip_atomic_store(p.part + (static_cast<int64_t>(split) * p.Mtot + m) * p.N +
+                                   tile * 16 + c,
+                               acc[mt][ct][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    return;
-  }
-  epilogue<T, MT, CT>(p, acc, lds, group, m0);
-}
-
-// Split-K finish: sums the S partial tiles of a column group in split order
-// (deterministic) and runs the fused epilogue.  A kernel boundary, not a
-// fence, orders the partial sums of all workgroups before this kernel.
-template <typename T, int MT, int CT>
-__global__ __launch_bounds__(256) void epilogue_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int ntiles = p.N / 16;
-  const int group = blockIdx.x;
-  const int m0 = blockIdx.z * (16 * MT);
-  f32x4 acc[MT][CT];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
+      int* ctr = p.cnt + blockIdx.z * ngroups + group;
+      const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == p.S - 1;
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int tile = (group * 4 + wave) * CT + ct;
+    for (int ct = 0; ct < CT; ++ct) {
+      const int tile = (group * 4 + wave) * CT + ct;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = m0 + mt * 16 + 4 * g + j;
-        float sum = 0.f;
-        if (m < p.M && tile < ntiles) {
-          for (int sp = 0; sp < p.S; ++sp)
-            sum += p.part[(static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c];
+        for (int j = 0; j < 4; ++j) {
+          const int m = m0 + mt * 16 + 4 * g + j;
+          float sum = 0.f;
+          if (m < p.M && tile < ntiles) {
+            for (int sp = 0; sp < p.S; ++sp)
+              sum += __hip_atomic_load(
+                  p.part + (static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c,
+                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          acc[mt][ct][j] = sum;
         }
-        acc[mt][ct][j] = sum;
-      }
+    }
   }
   epilogue<T, MT, CT>(p, acc, lds, group, m0);
 }
@@ -502,18 +507,19 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int rows = p.M < 64 ? p.M : 64;
   p.MT = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   const int chunks = (p.M + 16 * p.MT - 1) / (16 * p.MT);
-  // two 16-column tiles per wave for wide GEMMs (bf16 only: fp32 fragments
-  // take twice the registers)
-  p.CT = (!fp32 && ntiles >= 2 * num_cus) ? 2 : 1;
+  // one 16-column tile per wave; two only when there are far more tiles
+  // than the chip holds (bf16 only: fp32 fragments take twice the registers)
+  p.CT = (!fp32 && ntiles >= 16 * num_cus) ? 2 : 1;
   const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
   const int ksteps = (p.K + kStep - 1) / kStep;
   const int pmax = max_piece(p.MT);
-  // a split stages at most one piece; more splits while the grid is short of
-  // two workgroups per CU and each split keeps at least two steps
-  int S = (ksteps + pmax - 1) / pmax;
-  const int want = 2 * num_cus;
-  while (ngroups * chunks * S < want && (ksteps + S) / (S + 1) >= 2) ++S;
-  // the partial sums must fit the workspace; a split may then span pieces
+  // no K split when the column groups alone cover every CU; else split K
+  // until the grid holds about two workgroups per CU, each split keeping at
+  // least two steps
+  int S = 1;
+  if (ngroups * chunks < num_cus)
+    while (ngroups * chunks * S < 2 * num_cus && (ksteps + S) / (S + 1) >= 2) ++S;
+  // the partial sums must fit the workspace
   while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
   const int steps = (ksteps + S - 1) / S;
   p.KS = steps * kStep;
@@ -542,10 +548,6 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(ngroups * p.S, 1, chunks), dim3(256), lds, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.S == 1) return e;
-  hipLaunchKernelGGL((epilogue_kernel<T, MT, CT>), dim3(ngroups, 1, chunks), dim3(256),
-                     tile_bytes, s, p);
   return hipGetLastError();
 }
 
@@ -573,7 +575,8 @@ hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.N % 16 || p.K % 8 || p.K < 8 || p.KS % kStep || p.S < 1 ||
-      static_cast<int64_t>(p.S) * p.KS < p.K || (p.S > 1 && p.part == nullptr) ||
+      static_cast<int64_t>(p.S) * p.KS < p.K ||
+      (p.S > 1 && (p.part == nullptr || p.cnt == nullptr)) ||
       (p.CT == 2 && sizeof(T) != 2) || p.wpack == nullptr)
     return hipErrorInvalidValue;
   // a split either fits one piece or spans whole pieces of 4 or 8 steps

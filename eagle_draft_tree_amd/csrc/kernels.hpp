@@ -47,6 +47,7 @@ struct GemmParams {
   int Mtot = 0;                   // padded rows of the partial buffer
   float* part = nullptr;          // [S, Mtot, N] split-K partials
   int64_t part_elems = 0;         // capacity of part (floats)
+  int* cnt = nullptr;             // per (row chunk, column group) arrival counters (zero)
   int epi = EPI_STORE;
   void* out = nullptr;            // float activations (q: weight type)
   int64_t ldo = 0;
@@ -85,15 +86,15 @@ struct AttnParams {
   const void* q = nullptr;          // [rows, nq, hd]
   float* o = nullptr;               // [rows, nq, hd] float
   const void* kc = nullptr;         // [B, nkv, cap, hd]
-  const void* vc = nullptr;
+  const void* vc = nullptr;         // [B, nkv, hd, cap] (V stored transposed)
   const int32_t* tok = nullptr;     // row valid iff tok >= 0
   const int32_t* plen = nullptr;    // [rows]
   const int32_t* sbase = nullptr;   // [B]
   const uint64_t* smask = nullptr;  // [rows]
-  int nsplit = 1, chunk = 64;
+  int nsplit = 1;                   // prefix splits (plus one scratch split)
+  int split_keys = 64;              // keys per prefix split (multiple of 64)
   float* part_o = nullptr;          // [B, nkv, nsplit+1, QG, hd]
   float* part_ml = nullptr;         // [B, nkv, nsplit+1, QG, 2]
-  int* cnt = nullptr;               // [B, nkv]
   float scale = 1.f;
 };
 template <typename T> hipError_t launch_attention(const AttnParams& p, hipStream_t s);

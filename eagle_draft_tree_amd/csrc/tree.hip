@@ -29,20 +29,34 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
   const int ncand = p.ntile * K;
-  for (int idx = threadIdx.x; idx < ncand; idx += 256) {
-    const float v = p.cand_val[base * K + idx];
-    const int id = p.cand_id[base * K + idx];
-    if (!better(v, id, lv[K - 1], li[K - 1])) continue;
+  // candidates are fetched in batches of 8 per thread so their loads overlap
+  // (one at a time, each waits a full memory latency)
+  constexpr int kBatch = 8;
+  for (int b0 = threadIdx.x; b0 < ncand; b0 += 256 * kBatch) {
+    float bv[kBatch];
+    int bi[kBatch];
 #pragma unroll
-    for (int j = kMaxTopK - 1; j >= 0; --j) {
-      if (j >= K) continue;
-      if (better(v, id, lv[j], li[j])) {
-        if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
-          lv[j] = lv[j - 1];
-          li[j] = li[j - 1];
-        } else {
-          lv[j] = v;
-          li[j] = id;
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = b0 + u * 256;
+      bv[u] = idx < ncand ? p.cand_val[base * K + idx] : -INFINITY;
+      bi[u] = idx < ncand ? p.cand_id[base * K + idx] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float v = bv[u];
+      const int id = bi[u];
+      if (!better(v, id, lv[K - 1], li[K - 1])) continue;
+#pragma unroll
+      for (int j = kMaxTopK - 1; j >= 0; --j) {
+        if (j >= K) continue;
+        if (better(v, id, lv[j], li[j])) {
+          if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
+            lv[j] = lv[j - 1];
+            li[j] = li[j - 1];
+          } else {
+            lv[j] = v;
+            li[j] = id;
+          }
         }
       }
     }
@@ -67,12 +81,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   // log-sum-exp over tile statistics
   float M = -INFINITY, S = 0.f;
-  for (int t = threadIdx.x; t < p.ntile; t += 256) {
-    const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
-    if (mx == -INFINITY) continue;
-    const float nm = fmaxf(M, mx);
-    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
-    M = nm;
+  for (int t0 = threadIdx.x; t0 < p.ntile; t0 += 256 * 4) {
+    float mxs[4], ses[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * 256;
+      mxs[u] = t < p.ntile ? p.stat[(base + t) * 2] : -INFINITY;
+      ses[u] = t < p.ntile ? p.stat[(base + t) * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mx = mxs[u], se = ses[u];
+      if (mx == -INFINITY) continue;
+      const float nm = fmaxf(M, mx);
+      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
+      M = nm;
+    }
   }
   sm[threadIdx.x] = M;
   ss[threadIdx.x] = S;
@@ -636,23 +660,30 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
   if (tid == 0) p.kv_len[b] = len_out + nk;
   if (nk == 0) return;
   // gather every kept row first, then scatter: destinations can overlap
-  // sources of other kept rows
+  // sources of other kept rows.  K rows are [cap, hd]; V is stored
+  // transposed ([hd, cap]), so a V "row" is a column.
   extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
   const int n16 = p.hd * p.elem_bytes / 2;  // 16-bit units per row
+  const int u16 = p.elem_bytes / 2;         // 16-bit units per element
   for (int kvh = 0; kvh < p.nkv; ++kvh) {
+    const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
     for (int which = 0; which < 2; ++which) {
       uint16_t* cache = static_cast<uint16_t*>(which ? p.vc : p.kc);
-      const int64_t hb = (static_cast<int64_t>(b) * p.nkv + kvh) * p.cap;
+      auto at = [&](int row, int off) -> int64_t {
+        if (which == 0) return (bk * p.cap + row) * n16 + off;
+        const int d = off / u16, w = off % u16;
+        return ((bk * p.hd + d) * p.cap + row) * u16 + w;
+      };
       for (int e = tid; e < nk * n16; e += 256) {
         const int i = e / n16, off = e % n16;
         const int src = len_out + p.t_slot[ob + s_kept[i]];
-        s_rows[e] = (src >= 0 && src < p.cap) ? cache[(hb + src) * n16 + off] : 0;
+        s_rows[e] = (src >= 0 && src < p.cap) ? cache[at(src, off)] : 0;
       }
       __syncthreads();
       for (int e = tid; e < nk * n16; e += 256) {
         const int i = e / n16, off = e % n16;
         const int dst = p_root + p.t_depth[ob + s_kept[i]];
-        if (dst >= 0 && dst < p.cap) cache[(hb + dst) * n16 + off] = s_rows[e];
+        if (dst >= 0 && dst < p.cap) cache[at(dst, off)] = s_rows[e];
       }
       __syncthreads();
     }

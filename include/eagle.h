@@ -116,10 +116,14 @@ typedef struct {
 } eagle_weights;
 
 /* Draft KV cache ([M75] 0x03C: the drafter keeps its own K/V state,
- * separate from the target's): k, v [B, n_kv, cap, hd] in the config dtype.  Rows
- * [0, len) are committed; a draft call appends its seed rows there and uses
- * rows [len_out, len_out + (D-1)K) as tree scratch.  len_in is read,
- * len_out written, so a call can be replayed with the same inputs. */
+ * separate from the target's), config dtype: k [B, n_kv, cap, hd] (row r of
+ * a head is key r) and v [B, n_kv, hd, cap] (stored transposed: column r of
+ * a head is value r), so that tree attention reads both as matrix-core
+ * operands directly.  cap is a multiple of 8.  Rows [0, len) are committed;
+ * a draft call appends its seed rows there and uses rows
+ * [len_out, len_out + (D-1)K) as tree scratch.  len_in is read, len_out
+ * written, so a call can be replayed with the same inputs. */
+
 typedef struct {
   void *k;
   void *v;

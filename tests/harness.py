@@ -96,7 +96,7 @@ def make_seq(model, b, ctx, cap, run_oracle=True, record=False, max_attempts=50,
 
 def cap_for(cfg, ctx_max, rounds=1):
     extra = cfg.s_max + (cfg.D - 1) * cfg.K + rounds * (cfg.D + 2) + 64
-    return int(ctx_max + extra)
+    return int(ctx_max + extra + 7) // 8 * 8
 
 
 def upload_batch(model, seqs, cap, s_max=None):
@@ -107,7 +107,7 @@ def upload_batch(model, seqs, cap, s_max=None):
     S = s_max or cfg.s_max
     k = torch.stack([s.k for s in seqs]).cuda()
     v = torch.stack([s.v for s in seqs]).cuda()
-    kv = KVCache(k, v, torch.tensor([s.ctx for s in seqs], dtype=torch.int32).cuda())
+    kv = KVCache.from_rows(k, v, torch.tensor([s.ctx for s in seqs], dtype=torch.int32).cuda())
     low = torch.stack([s.low for s in seqs]).cuda()
     mid = torch.stack([s.mid for s in seqs]).cuda()
     high = torch.stack([s.high for s in seqs]).cuda()

@@ -54,7 +54,7 @@ def _model(key, cfg, embed_rows=None):
 def _first_round(m, B, cap_rounds=1, d2t=None, s_max=None, **shape_kw):
     cfg = m.cfg.replace(B=B)
     ctxs = synth.contexts(cfg)
-    cap = cap_for(cfg, int(ctxs.max()), rounds=cap_rounds) + (s_max or 0)
+    cap = cap_for(cfg, int(ctxs.max()) + (s_max or 0), rounds=cap_rounds)
     seqs = [make_seq(m, b, int(ctxs[b]), cap, d2t=d2t) for b in range(B)]
     d = m.drafter(max_batch=B, **({"max_seed": s_max} if s_max else {}), **shape_kw)
     kv, feats, tok, seed_len = upload_batch(m, seqs, cap, s_max=d.shape.max_seed)
@@ -164,7 +164,7 @@ def _run_chain(m, seqs, d, kv, tree, rounds, T, mode, d2t=None, TV=None):
             assert int(kv_len[b]) == c.new_len
             _close(cfg, as_np(kv.k[b, :, :c.new_len].cpu()), c.kv.k[:, :c.new_len],
                    "k after commit")
-            _close(cfg, as_np(kv.v[b, :, :c.new_len].cpu()), c.kv.v[:, :c.new_len],
+            _close(cfg, as_np(kv.v_rows()[b, :, :c.new_len].cpu()), c.kv.v[:, :c.new_len],
                    "v after commit")
         if rnd == rounds - 1:
             break

@@ -79,7 +79,8 @@ def test_draft_step_parity(name):
     pos = np.array([ctxs[r // rps] + r % rps for r in range(B * rps)], np.int32)
     plen = pos + 1
     from eagle_draft_tree_amd import KVCache
-    kv = KVCache(K_all.cuda(), V_all.cuda(), torch.tensor(ctxs, dtype=torch.int32).cuda())
+    kv = KVCache.from_rows(K_all.cuda(), V_all.cuda(),
+                           torch.tensor(ctxs, dtype=torch.int32).cuda())
     zero_mask = torch.zeros(B * rps, dtype=torch.int64, device="cuda")
     a, tid, tval, lse = d.draft_step(
         B, rps, src.cuda(), torch.from_numpy(toks).cuda(),
@@ -109,7 +110,7 @@ def test_draft_step_parity(name):
         got_k = as_np(kv.k[b].cpu())
         for r in rows:
             _close(cfg, got_k[:, pos[r]], okv.k[:, pos[r]], "k row")
-            _close(cfg, as_np(kv.v[b].cpu())[:, pos[r]], okv.v[:, pos[r]], "v row")
+            _close(cfg, as_np(kv.v_rows()[b].cpu())[:, pos[r]], okv.v[:, pos[r]], "v row")
         # prefix untouched
         assert torch.equal(kv.k[b, :, :ctxs[b]].cpu(), K_all[b, :, :ctxs[b]])
 
@@ -133,7 +134,7 @@ def _run_tree_case(name, check_kv=True):
             lo = s.ctx + 1
             hi = lo + (cfg.D - 1) * cfg.K
             _close(cfg, as_np(kv.k[b, :, s.ctx:hi].cpu()), s.kv.k[:, s.ctx:hi], "k")
-            _close(cfg, as_np(kv.v[b, :, s.ctx:hi].cpu()), s.kv.v[:, s.ctx:hi], "v")
+            _close(cfg, as_np(kv.v_rows()[b, :, s.ctx:hi].cpu()), s.kv.v[:, s.ctx:hi], "v")
     return m, seqs, d, kv, tree
 
 
@@ -171,7 +172,7 @@ def test_verify_greedy_parity_with_commit(name):
         assert list(res["seed_rows"][b, :n].cpu().numpy()) == srows
         assert list(res["seed_tokens"][b, :n].cpu().numpy()) == stoks
         _close(cfg, as_np(kv.k[b, :, :new_len].cpu()), okv.k[:, :new_len], "k commit")
-        _close(cfg, as_np(kv.v[b, :, :new_len].cpu()), okv.v[:, :new_len], "v commit")
+        _close(cfg, as_np(kv.v_rows()[b, :, :new_len].cpu()), okv.v[:, :new_len], "v commit")
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 1.0), ("tiny", 0.6), ("mid", 1.0)])
@@ -231,9 +232,10 @@ def test_device_status_capacity():
     cfg = m.cfg
     d = m.drafter()
     from eagle_draft_tree_amd import KVCache
-    cap = cfg.ctx[0] + 3      # needs ctx + 1 + (D-1)K rows
+    cap = cfg.ctx[0] + 8      # needs ctx + 1 + (D-1)K rows
+    assert cap < cfg.ctx[0] + 1 + (cfg.D - 1) * cfg.K
     k = torch.zeros(1, cfg.n_kv, cap, cfg.hd, dtype=tdtype(cfg), device="cuda")
-    kv = KVCache(k, torch.zeros_like(k),
+    kv = KVCache.from_rows(k, torch.zeros_like(k),
                  torch.tensor([cfg.ctx[0]], dtype=torch.int32, device="cuda"))
     src = torch.zeros(1, cfg.s_max, cfg.H, dtype=tdtype(cfg), device="cuda")
     tok = torch.tensor([[5, -1]], dtype=torch.int32, device="cuda")

@@ -136,8 +136,9 @@ class Drafter:
             pass
 
     # ------------------------------------------------------------------
-    def profile(self, on: bool):
-        check(lib().eagle_profile(self._ctx, 1 if on else 0), "eagle_profile")
+    def profile(self, on: bool, resume: bool = False):
+        mode = (2 if resume else 1) if on else 0
+        check(lib().eagle_profile(self._ctx, mode), "eagle_profile")
 
     def profile_read(self) -> dict:
         import numpy as np

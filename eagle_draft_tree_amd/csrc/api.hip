@@ -175,7 +175,7 @@ Offsets make_layout(const eagle_config& c) {
 
 // Optional per-launch timing: HIP events around each kernel of a context.
 struct Profiler {
-  static constexpr int kPairs = 4096;
+  static constexpr int kPairs = 8192;
   bool on = false;
   int used = 0;
   bool overflow = false;
@@ -854,9 +854,14 @@ eagle_status eagle_profile(eagle_ctx* ctx, int32_t on) {
       if (hipEventCreate(&p.ev[i]) != hipSuccess) return EAGLE_EHIP;
     p.created = true;
   }
+  // 1 starts a new record, 2 resumes the current one, 0 stops (the record
+  // stays for eagle_profile_read)
+  if (on < 0 || on > 2) return EAGLE_EINVAL;
+  if (on == 1) {
+    p.used = 0;
+    p.overflow = false;
+  }
   p.on = on != 0;
-  p.used = 0;
-  p.overflow = false;
   return EAGLE_OK;
 }
 

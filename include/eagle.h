@@ -303,12 +303,15 @@ eagle_status eagle_draw_uniforms(uint64_t seed, uint64_t stream_id,
                                  int32_t draws, float *out, hipStream_t stream);
 
 /* Measurement hook.  While profiling is on, every kernel the context enqueues
- * is bracketed by a pair of HIP events on its stream (up to 4096 launches
- * between reads).  eagle_profile(ctx, 1) clears the record and starts;
- * eagle_profile(ctx, 0) stops.  eagle_profile_read synchronises on the last
- * event and returns, per kernel class, the summed event time (ms), launch
- * count, algorithmic bytes (weights once + activations in/out; the target
- * logits for verification) and algorithmic flops, then clears the record.
+ * is bracketed by a pair of HIP events on its stream (up to 8192 launches
+ * between reads).  eagle_profile(ctx, 1) clears the record and starts,
+ * eagle_profile(ctx, 2) resumes adding to it, eagle_profile(ctx, 0) stops
+ * and keeps it (so a caller can sample some launches of a longer run); other
+ * values are EINVAL.  eagle_profile_read
+ * synchronises on the last event and returns, per kernel class, the summed
+ * event time (ms), launch count, algorithmic bytes (weights once +
+ * activations in/out; the target logits for verification) and algorithmic
+ * flops, then clears the record.
  * Classes: 0 draft-layer GEMMs, 1 fusion GEMM, 2 tree attention, 3 LM-head
  * top-k merge, 4 tree growth/rerank/flatten, 5 verification.  Returns
  * EWORKSPACE if launches were dropped because the record was full. */

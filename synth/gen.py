@@ -81,6 +81,9 @@ CONFIGS = {
                       T=0.0, **_70B),
     "70b_bs16": Config("70b_bs16", B=16, ctx=(4096, 4096), D=6, K=10, N=60,
                        T=1.0, **_70B),
+    # chain drafting (top-1 per step, depth 3) at batch 16
+    "8b_chain_bs16": Config("8b_chain_bs16", B=16, ctx=(512, 4096), D=3, K=1,
+                            N=3, T=0.0, **_8B),
     # long-context reasoning shape: 16k prefix, 64 chained rounds
     "long_bs8": Config("long_bs8", B=8, ctx=(16384, 16384), D=8, K=8, N=80,
                        T=0.6, rounds=64, **_8B),

@@ -243,3 +243,89 @@ class ChainSeq:
         self.taps = taps
         self.len_out = self.new_len + len(self.seed_rows)
         return att
+
+
+def close(cfg, got, want, what=""):
+    atol, rtol = tol(cfg)
+    np.testing.assert_allclose(got, want, atol=atol, rtol=rtol, err_msg=what)
+
+
+def first_round(m, B, cap_rounds=1, d2t=None, s_max=None, check=None, **shape_kw):
+    """Seeded sequences for m.cfg at batch B (contexts drawn as the config
+    says), their oracle trees, and the library's first round checked
+    against them: fuse, draft_tree, len_out and the tree arrays.  With
+    `check`, only those sequences get an oracle tree and are compared."""
+    cfg = m.cfg.replace(B=B)
+    ctxs = synth.contexts(cfg)
+    cap = cap_for(cfg, int(ctxs.max()) + (s_max or 0), rounds=cap_rounds)
+    seqs = []
+    for b in range(B):
+        on = check is None or b in check
+        seqs.append(make_seq(m, b, int(ctxs[b]), cap, run_oracle=on, d2t=d2t))
+        if on:
+            print(f"[oracle] sequence {b} ctx {int(ctxs[b])} tree built", flush=True)
+    d = m.drafter(max_batch=B, **({"max_seed": s_max} if s_max else {}), **shape_kw)
+    kv, feats, tok, seed_len = upload_batch(m, seqs, cap, s_max=d.shape.max_seed)
+    g, tree, len_out = gpu_tree_round(d, m, seqs, kv, feats, tok, seed_len)
+    for b, s in enumerate(seqs):
+        assert int(len_out[b]) == s.ctx + 1
+        if s.tree is not None:
+            assert_tree_equal(m.cfg, tree_to_np(tree, b), s.tree)
+    return seqs, d, kv, tree
+
+
+def run_chain(m, seqs, d, kv, tree, rounds, T, mode, d2t=None, TV=None):
+    """`rounds` chained rounds on the GPU against the oracle's ChainSeq:
+    verify (accept lengths, tokens), commit (seed rows and tokens, new
+    length, committed K/V rows), then fuse the next seed rows and draft the
+    next tree (tree arrays).  Sequences with odd b get the target as drawn;
+    even b get a target leaning towards each row's best child."""
+    from eagle_draft_tree_amd import COMMIT_KEEP, COMMIT_RESEED
+    cfg = m.cfg
+    B, S = len(seqs), d.shape.max_seed
+    chains = [ChainSeq(m, s, T, mode, d2t, TV, boost=0.0 if s.b % 2 else 8.0)
+              for s in seqs]
+    kv_len = torch.empty(B, dtype=torch.int32, device="cuda")
+    accepted = 0
+    for rnd in range(rounds):
+        outs = [c.verify(rnd) for c in chains]
+        tl = np.stack([o[0] for o in outs])
+        res = d.verify(tree, torch.from_numpy(tl).cuda(), T, seed=SEED,
+                       round=rnd, kv=kv, kv_len_out=kv_len,
+                       commit_mode=COMMIT_RESEED if mode == "reseed" else COMMIT_KEEP)
+        torch.cuda.synchronize()
+        for b, c in enumerate(chains):
+            want = outs[b][1]
+            accepted += want["accept_len"]
+            assert int(res["accept_len"][b]) == want["accept_len"], (rnd, b)
+            assert np.array_equal(res["tokens"][b].cpu().numpy(), want["tokens"])
+            n = int(res["seed_len"][b])
+            assert n == len(c.seed_rows), (rnd, b)
+            assert list(res["seed_rows"][b, :n].cpu().numpy()) == c.seed_rows
+            assert list(res["seed_tokens"][b, :n].cpu().numpy()) == c.seed_toks
+            assert int(kv_len[b]) == c.new_len
+            close(cfg, as_np(kv.k[b, :, :c.new_len].cpu()), c.kv.k[:, :c.new_len],
+                   "k after commit")
+            close(cfg, as_np(kv.v_rows()[b, :, :c.new_len].cpu()), c.kv.v[:, :c.new_len],
+                   "v after commit")
+        if rnd == rounds - 1:
+            break
+        atts = [c.draft(rnd) for c in chains]
+        low = torch.zeros(B * S, cfg.H, dtype=kv.k.dtype)
+        mid, high = low.clone(), low.clone()
+        for b, c in enumerate(chains):
+            for i in range(len(c.seed_rows)):
+                for t, arr in zip((low, mid, high), c.taps):
+                    t[b * S + i] = stored(cfg, arr[i])
+        g = d.fuse(low.cuda(), mid.cuda(), high.cuda())
+        seed_src = g.view(B, S, cfg.H)
+        kv.length.copy_(kv_len)
+        tree, len_out = d.draft_tree(seed_src, res["seed_tokens"].contiguous(),
+                                     res["seed_len"], kv)
+        torch.cuda.synchronize()
+        for b, c in enumerate(chains):
+            assert int(len_out[b]) == c.len_out
+            assert_tree_equal(cfg, tree_to_np(tree, b), c.tree)
+        print(f"[chain] round {rnd + 1} trees equal (attempts {atts})", flush=True)
+    print(f"[chain] T={T} mode={mode}: accepted {accepted} over {rounds} rounds",
+          flush=True)

@@ -8,18 +8,11 @@ import torch
 
 import oracle as O
 import synth
-from harness import (SEED, ChainSeq, Model, as_np, assert_tree_equal, cap_for,
-                     gpu_tree_round, make_seq, stored, tol, tree_to_np,
-                     upload_batch)
+from harness import SEED, Model, first_round, run_chain, stored
 
 pytestmark = pytest.mark.gpu
 
 MID = dict(H=1024, n_q=8, n_kv=2, hd=128, F=2816, V=8000, ctx=(200, 700))
-
-
-def _close(cfg, got, want, what=""):
-    atol, rtol = tol(cfg)
-    np.testing.assert_allclose(got, want, atol=atol, rtol=rtol, err_msg=what)
 
 
 def test_philox_draws_match_oracle_on_a_million_counters():
@@ -51,27 +44,13 @@ def _model(key, cfg, embed_rows=None):
     return _models[key]
 
 
-def _first_round(m, B, cap_rounds=1, d2t=None, s_max=None, **shape_kw):
-    cfg = m.cfg.replace(B=B)
-    ctxs = synth.contexts(cfg)
-    cap = cap_for(cfg, int(ctxs.max()) + (s_max or 0), rounds=cap_rounds)
-    seqs = [make_seq(m, b, int(ctxs[b]), cap, d2t=d2t) for b in range(B)]
-    d = m.drafter(max_batch=B, **({"max_seed": s_max} if s_max else {}), **shape_kw)
-    kv, feats, tok, seed_len = upload_batch(m, seqs, cap, s_max=d.shape.max_seed)
-    g, tree, len_out = gpu_tree_round(d, m, seqs, kv, feats, tok, seed_len)
-    for b, s in enumerate(seqs):
-        assert int(len_out[b]) == s.ctx + 1
-        assert_tree_equal(m.cfg, tree_to_np(tree, b), s.tree)
-    return seqs, d, kv, tree
-
-
 @pytest.mark.parametrize("B", [2, 16, 64])
 def test_chain_mode_top1(B):
     """Chain drafting (K = 1, depth 3): the tree is a single path, verified
     greedily and by seeded sampling."""
     m = _model("chain", synth.config("8b_bs1", **MID, K=1, D=3, N=3))
     cfg = m.cfg
-    seqs, d, kv, tree = _first_round(m, B)
+    seqs, d, kv, tree = first_round(m, B)
     print(f"[chain] B={B} trees equal", flush=True)
     for T in (0.0, 1.0):
         tl = []
@@ -104,8 +83,8 @@ def test_reseed_commit_and_next_draft():
     next round, and the next draft over those seeds matches the oracle."""
     cfg0 = synth.config("8b_bs1", **MID, K=4, D=3, N=10)
     m = _model("reseed", cfg0)
-    seqs, d, kv, tree = _first_round(m, 3, cap_rounds=2, s_max=cfg0.D + 1)
-    _run_chain(m, seqs, d, kv, tree, rounds=3, T=1.0, mode="reseed")
+    seqs, d, kv, tree = first_round(m, 3, cap_rounds=2, s_max=cfg0.D + 1)
+    run_chain(m, seqs, d, kv, tree, rounds=3, T=1.0, mode="reseed")
 
 
 @pytest.mark.parametrize("T,mode", [(0.6, "keep"), (0.0, "keep"), (0.6, "reseed")])
@@ -114,8 +93,8 @@ def test_chained_rounds(T, mode):
     cfg0 = synth.config("8b_bs1", **MID, K=4, D=4, N=12)
     m = _model("chained", cfg0)
     s_max = cfg0.D + 1 if mode == "reseed" else 2
-    seqs, d, kv, tree = _first_round(m, 3, cap_rounds=6, s_max=s_max)
-    _run_chain(m, seqs, d, kv, tree, rounds=5, T=T, mode=mode)
+    seqs, d, kv, tree = first_round(m, 3, cap_rounds=6, s_max=s_max)
+    run_chain(m, seqs, d, kv, tree, rounds=5, T=T, mode=mode)
 
 
 def test_reduced_draft_vocabulary():
@@ -129,61 +108,9 @@ def test_reduced_draft_vocabulary():
     d2t = np.sort(rng.choice(TV, size=cfg0.V, replace=False)).astype(np.int64)
     m.gpu["d2t"] = torch.from_numpy(d2t.astype(np.int32)).cuda()
     try:
-        seqs, d, kv, tree = _first_round(m, 3, cap_rounds=3, d2t=d2t,
+        seqs, d, kv, tree = first_round(m, 3, cap_rounds=3, d2t=d2t,
                                          target_vocab=TV)
-        _run_chain(m, seqs, d, kv, tree, rounds=2, T=1.0, mode="keep",
+        run_chain(m, seqs, d, kv, tree, rounds=2, T=1.0, mode="keep",
                    d2t=d2t, TV=TV)
     finally:
         m.gpu.pop("d2t")
-
-
-def _run_chain(m, seqs, d, kv, tree, rounds, T, mode, d2t=None, TV=None):
-    from eagle_draft_tree_amd import COMMIT_KEEP, COMMIT_RESEED
-    cfg = m.cfg
-    B, S = len(seqs), d.shape.max_seed
-    chains = [ChainSeq(m, s, T, mode, d2t, TV, boost=0.0 if s.b % 2 else 8.0)
-              for s in seqs]
-    kv_len = torch.empty(B, dtype=torch.int32, device="cuda")
-    accepted = 0
-    for rnd in range(rounds):
-        outs = [c.verify(rnd) for c in chains]
-        tl = np.stack([o[0] for o in outs])
-        res = d.verify(tree, torch.from_numpy(tl).cuda(), T, seed=SEED,
-                       round=rnd, kv=kv, kv_len_out=kv_len,
-                       commit_mode=COMMIT_RESEED if mode == "reseed" else COMMIT_KEEP)
-        torch.cuda.synchronize()
-        for b, c in enumerate(chains):
-            want = outs[b][1]
-            accepted += want["accept_len"]
-            assert int(res["accept_len"][b]) == want["accept_len"], (rnd, b)
-            assert np.array_equal(res["tokens"][b].cpu().numpy(), want["tokens"])
-            n = int(res["seed_len"][b])
-            assert n == len(c.seed_rows), (rnd, b)
-            assert list(res["seed_rows"][b, :n].cpu().numpy()) == c.seed_rows
-            assert list(res["seed_tokens"][b, :n].cpu().numpy()) == c.seed_toks
-            assert int(kv_len[b]) == c.new_len
-            _close(cfg, as_np(kv.k[b, :, :c.new_len].cpu()), c.kv.k[:, :c.new_len],
-                   "k after commit")
-            _close(cfg, as_np(kv.v_rows()[b, :, :c.new_len].cpu()), c.kv.v[:, :c.new_len],
-                   "v after commit")
-        if rnd == rounds - 1:
-            break
-        atts = [c.draft(rnd) for c in chains]
-        low = torch.zeros(B * S, cfg.H, dtype=kv.k.dtype)
-        mid, high = low.clone(), low.clone()
-        for b, c in enumerate(chains):
-            for i in range(len(c.seed_rows)):
-                for t, arr in zip((low, mid, high), c.taps):
-                    t[b * S + i] = stored(cfg, arr[i])
-        g = d.fuse(low.cuda(), mid.cuda(), high.cuda())
-        seed_src = g.view(B, S, cfg.H)
-        kv.length.copy_(kv_len)
-        tree, len_out = d.draft_tree(seed_src, res["seed_tokens"].contiguous(),
-                                     res["seed_len"], kv)
-        torch.cuda.synchronize()
-        for b, c in enumerate(chains):
-            assert int(len_out[b]) == c.len_out
-            assert_tree_equal(cfg, tree_to_np(tree, b), c.tree)
-        print(f"[chain] round {rnd + 1} trees equal (attempts {atts})", flush=True)
-    print(f"[chain] T={T} mode={mode}: accepted {accepted} over {rounds} rounds",
-          flush=True)

@@ -14,6 +14,7 @@ CPU oracle on the same seeded inputs:
 Every tree array is bit-exact, every accepted length and token equal, and
 draft states, scores and committed K/V rows within the bf16 tolerance.  The
 oracle runs in float64 on the host and dominates the run time."""
+import copy
 import gc
 
 import numpy as np
@@ -28,15 +29,27 @@ pytestmark = pytest.mark.gpu
 _held = {}
 
 
+def _dims(cfg):
+    return (cfg.H, cfg.n_q, cfg.n_kv, cfg.hd, cfg.F, cfg.V, cfg.dtype)
+
+
 def _model(name):
-    """One model at a time: the 70B drafter's float64 oracle copy is 14 GB."""
-    if name not in _held:
+    """One set of weights at a time (the 70B drafter's float64 oracle copy
+    is 14 GB); workloads with the same drafter dimensions share it, each
+    seeing its own batch, context and tree settings."""
+    cfg = synth.config(name)
+    base = _held.get("base")
+    if base is None or _dims(base.cfg) != _dims(cfg):
         _held.clear()
         gc.collect()
         torch.cuda.empty_cache()
-        print(f"[setup] model {name}", flush=True)
-        _held[name] = Model(synth.config(name))
-    return _held[name]
+        print(f"[setup] weights for {name}", flush=True)
+        base = _held["base"] = Model(cfg)
+    m = copy.copy(base)
+    m.cfg = cfg
+    m.oracle = copy.copy(base.oracle)
+    m.oracle.cfg = cfg
+    return m
 
 
 def test_8b_bs1_two_rounds_greedy():
@@ -51,6 +64,15 @@ def test_8b_bs64_sampling_every_sequence():
     seqs, d, kv, tree = first_round(m, 64)
     print("[8b bs64] 64 trees equal", flush=True)
     run_chain(m, seqs, d, kv, tree, rounds=1, T=1.0, mode="keep")
+
+
+def test_long_context_bs8_four_chained_rounds():
+    m = _model("long_bs8")
+    seqs, d, kv, tree = first_round(m, 8, cap_rounds=5)
+    for b in range(8):
+        assert_tree_equal(m.cfg, tree_to_np(tree, b), seqs[b].tree)
+    print("[long bs8] 8 trees equal (two mask words per row)", flush=True)
+    run_chain(m, seqs, d, kv, tree, rounds=4, T=0.6, mode="keep")
 
 
 def test_70b_bs1_greedy():
@@ -90,12 +112,3 @@ def test_70b_bs16_subset_sampling():
         close(cfg, as_np(kv.v_rows()[b, :, :c.new_len].cpu()), c.kv.v[:, :c.new_len], "v")
     # the unchecked sequences verified without error
     assert (res["accept_len"] >= 0).all()
-
-
-def test_long_context_bs8_four_chained_rounds():
-    m = _model("long_bs8")
-    seqs, d, kv, tree = first_round(m, 8, cap_rounds=5)
-    for b in range(8):
-        assert_tree_equal(m.cfg, tree_to_np(tree, b), seqs[b].tree)
-    print("[long bs8] 8 trees equal (two mask words per row)", flush=True)
-    run_chain(m, seqs, d, kv, tree, rounds=4, T=0.6, mode="keep")

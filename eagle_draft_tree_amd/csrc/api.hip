@@ -39,8 +39,8 @@ struct Offsets {
       lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
       c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
       len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
-      cnt_gemm, pack[7];
-  int R, Rpad, ncnt, ntile_lm, qg, ncand, max_split;
+      cnt_gemm, pack[7], apack;
+  int R, Rpad, ncnt, ntile_lm, qg, ncand, max_split, apack_rows;
   int64_t part_elems;
   size_t total;
 };
@@ -124,6 +124,13 @@ Offsets make_layout(const eagle_config& c) {
   const int maxN = std::max(std::max(V, 2 * F), std::max(3 * H, qd + 2 * kd));
   f.part_elems = static_cast<int64_t>(16) * std::min<int64_t>(R, 32) * maxN;
   f.part = L.take(static_cast<size_t>(f.part_elems) * 4);
+  // dense path (bf16, more than 64 rows): A as packed bf16 hi/lo fragments,
+  // 4 bytes per element of the widest K
+  f.apack_rows = (c.dtype == EAGLE_BF16 && f.R > 64) ? (f.R + 63) / 64 * 64 : 0;
+  {
+    const int kmax = std::max(std::max(3 * H, F), qd);
+    f.apack = L.take(static_cast<size_t>(f.apack_rows) * ((kmax + 127) / 128 * 128) * 4);
+  }
   f.ntile_lm = (V + 63) / 64;
   f.lm_val = L.take(R * f.ntile_lm * c.topk * 4);
   f.lm_id = L.take(R * f.ntile_lm * c.topk * 4);
@@ -250,6 +257,8 @@ hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEM
   p.part_elems = c->off.part_elems;
   p.cnt = c->at<int>(c->off.cnt_gemm);
   p.eps = c->cfg.rms_eps;
+  p.apack = c->off.apack_rows > 0 ? c->at<char>(c->off.apack) : nullptr;
+  p.apack_rows = c->off.apack_rows;
   plan_gemm(p, c->num_cus, sizeof(T) == 4);
   // algorithmic bytes: weights once, activation rows in, results out
   const double w_bytes = static_cast<double>(p.N) * p.K * sizeof(T);

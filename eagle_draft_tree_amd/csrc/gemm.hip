@@ -99,6 +99,54 @@ __device__ __forceinline__ void row_factors(const GemmParams& p, float* rn, int 
   if (part == 0) rn[r] = 1.f / sqrtf(q / static_cast<float>(sg.width) + p.eps);
 }
 
+// Value of A[row m0 + m][k .. k+7] as the GEMM multiplies it: the row of the
+// segment holding k (gathered through its row index), times the RMSNorm
+// factor and gain when segment 0 is normalised; zero past M, K or a gather
+// out of range.
+template <typename T>
+__device__ __forceinline__ void a_values(const GemmParams& p, const float* rn, int m,
+                                         int row, int k, int kend, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  if (row >= p.M || k >= kend) return;
+  int si = 0, base = 0;
+  if (p.nseg > 1 && k >= p.seg[0].width) {
+    base = p.seg[0].width;
+    si = 1;
+    if (p.nseg > 2 && k >= base + p.seg[1].width) {
+      base += p.seg[1].width;
+      si = 2;
+    }
+  }
+  const ASeg& sg = si == 0 ? p.seg[0] : (si == 1 ? p.seg[1] : p.seg[2]);
+  int r = row;
+  if (sg.rowidx != nullptr) {
+    r = sg.rowidx[row];
+    if (r < 0 || r >= sg.rowlimit) return;
+  }
+  const int kk = k - base;
+  load8<T>(sg, r, kk, v);
+  if (sg.f32 && sg.ss != nullptr) {
+    const float f = rn[m];
+    Frag8<T> gv;
+    gv.load(static_cast<const T*>(sg.gain) + kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
+  }
+}
+
+// bf16 hi + lo parts of 8 fp32 values (hi = nearest bf16, lo = the rest)
+__device__ __forceinline__ void split_hi_lo(const float (&v)[8], u32x4& hi_out, u32x4& lo_out) {
+  Frag8<uint16_t> hi, lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi.set_pair(j, v[2 * j], v[2 * j + 1]);
+    lo.set_pair(j, v[2 * j] - hi.get(2 * j), v[2 * j + 1] - hi.get(2 * j + 1));
+  }
+  hi_out = hi.v;
+  lo_out = lo.v;
+}
+
 // Stage rows [m0, m0 + 16 MT) x k in [k0, kend) of A in LDS, fragment order:
 // block ((s * 4 + e) * MT + mt) holds, for each lane (g, c), the 8 values of
 // row mt*16 + c at k = k0 + s*128 + g*32 + e*8.  bf16: hi at lane*16 and lo
@@ -111,53 +159,18 @@ __device__ __forceinline__ void fill_a(const GemmParams& p, unsigned char* lds, 
   const int total = MT * 16 * k8n;
   for (int idx = threadIdx.x; idx < total; idx += 256) {
     const int m = idx / k8n, k8 = idx - m * k8n;
-    const int k = k0 + 8 * k8;
-    const int row = m0 + m;
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    if (row < p.M && k < kend) {
-      int si = 0, base = 0;
-      if (p.nseg > 1 && k >= p.seg[0].width) {
-        base = p.seg[0].width;
-        si = 1;
-        if (p.nseg > 2 && k >= base + p.seg[1].width) {
-          base += p.seg[1].width;
-          si = 2;
-        }
-      }
-      const ASeg& sg = si == 0 ? p.seg[0] : (si == 1 ? p.seg[1] : p.seg[2]);
-      int r = row;
-      if (sg.rowidx != nullptr) {
-        r = sg.rowidx[row];
-        if (r < 0 || r >= sg.rowlimit) r = -1;
-      }
-      if (r >= 0) {
-        const int kk = k - base;
-        load8<T>(sg, r, kk, v);
-        if (sg.f32 && sg.ss != nullptr) {
-          const float f = rn[m];
-          Frag8<T> gv;
-          gv.load(static_cast<const T*>(sg.gain) + kk);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
-        }
-      }
-    }
+    a_values<T>(p, rn, m, m0 + m, k0 + 8 * k8, kend, v);
     const int s = k8 >> 4, rem = k8 & 15;
     const int g = rem >> 2, e = rem & 3;
     const int mt = m >> 4, c = m & 15;
     const int lane = g * 16 + c;
     unsigned char* blk = lds + static_cast<size_t>((s * 4 + e) * MT + mt) * kBlk;
     if constexpr (sizeof(T) == 2) {
-      Frag8<uint16_t> hi, lo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi.set_pair(j, v[2 * j], v[2 * j + 1]);
-        lo.set_pair(j, v[2 * j] - hi.get(2 * j), v[2 * j + 1] - hi.get(2 * j + 1));
-      }
-      *reinterpret_cast<u32x4*>(blk + lane * 16) = hi.v;
-      *reinterpret_cast<u32x4*>(blk + 1024 + lane * 16) = lo.v;
+      u32x4 hi, lo;
+      split_hi_lo(v, hi, lo);
+      *reinterpret_cast<u32x4*>(blk + lane * 16) = hi;
+      *reinterpret_cast<u32x4*>(blk + 1024 + lane * 16) = lo;
     } else {
       *reinterpret_cast<f32x4*>(blk + lane * 32) = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4*>(blk + lane * 32 + 16) = f32x4{v[4], v[5], v[6], v[7]};
@@ -170,6 +183,40 @@ __device__ __forceinline__ void fill_a(const GemmParams& p, unsigned char* lds, 
 }
 
 }  // namespace
+
+// One element of the QKV epilogue: RoPE on q and k columns (partner column
+// value `other`, frequency inv), then q to the q buffer, k to cache row
+// dest[m] and v to column dest[m] of the transposed V cache.
+template <typename T>
+__device__ __forceinline__ void qkv_element(const GemmParams& p, int m, int col, int c, float x,
+                                         float other, double inv) {
+  if (m >= p.M || p.tok[m] < 0) return;
+  const int hh = col / p.hd, cin = col % p.hd;
+  float y = x;
+  if (hh < p.nq + p.nkv) {
+    double sd, cd;
+    sincos(static_cast<double>(p.pos[m]) * inv, &sd, &cd);
+    const float cs = static_cast<float>(cd), sn = static_cast<float>(sd);
+    y = (c < 8) ? (x * cs - other * sn) : (x * cs + other * sn);
+  }
+  const T v = Elem<T>::from_f(y);
+  if (hh < p.nq) {
+    static_cast<T*>(p.out)[m * p.ldo + col] = v;
+    return;
+  }
+  const int b = m / p.rows_per_seq;
+  const int d = p.dest[m];
+  if (b >= p.batch || d < 0 || d >= p.cap) {
+    if (p.status != nullptr) atomicOr(p.status, 1 << 4);
+    return;
+  }
+  const bool isk = hh < p.nq + p.nkv;
+  const int kvh = isk ? hh - p.nq : hh - p.nq - p.nkv;
+  const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
+  // K rows [cap, hd]; V stored transposed, [hd, cap]
+  if (isk) static_cast<T*>(p.kc)[(bk * p.cap + d) * p.hd + cin] = v;
+  else static_cast<T*>(p.vc)[(bk * p.hd + cin) * p.cap + d] = v;
+}
 
 // Fused epilogue on the accumulators of one workgroup tile (column group
 // `group`, rows m0 .. m0 + 16 MT), lane layout of the 16x16 MFMA: lane
@@ -225,6 +272,33 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
     return;
   }
 
+  if (p.epi == EPI_QKV) {
+    // values and RoPE partners first, in a loop small enough to unroll;
+    // then the element work, whose double-precision sincos would keep a
+    // loop over the accumulators from unrolling (and put them in scratch)
+    float xs[CT][4 * MT], os[CT][4 * MT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xs[ct][mt * 4 + j] = acc[mt][ct][j];
+          os[ct][mt * 4 + j] = shfl_xor(acc[mt][ct][j], 8);
+        }
+    for (int ct = 0; ct < CT; ++ct) {
+      const int tile = (group * 4 + wave) * CT + ct;
+      if (tile >= ntiles) continue;
+      const int col = tile_col(p, tile, c);
+      const int fi = (col % p.hd) % (p.hd / 2);
+      const double inv = pow(static_cast<double>(p.theta),
+                             -2.0 * static_cast<double>(fi) / static_cast<double>(p.hd));
+      for (int i = 0; i < 4 * MT; ++i)
+        qkv_element<T>(p, m0 + (i >> 2) * 16 + 4 * g + (i & 3), col, c, xs[ct][i], os[ct][i], inv);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int tile = (group * 4 + wave) * CT + ct;
@@ -260,50 +334,70 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
           const float other = shfl_xor(acc[mt][ct][j], 8);
           if (c < 8 && m < p.M) out[m * p.ldo + f] = silu(acc[mt][ct][j]) * other;
         }
-    } else if (p.epi == EPI_QKV) {
-      const int col = tile_col(p, tile, c);
-      const int hh = col / p.hd, cin = col % p.hd;
-      const int half = p.hd / 2;
-      const bool rot = hh < p.nq + p.nkv;
-      const int fi = cin % half;
-      const double inv = pow(static_cast<double>(p.theta),
-                             -2.0 * static_cast<double>(fi) / static_cast<double>(p.hd));
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + mt * 16 + 4 * g + j;
-          const float x = acc[mt][ct][j];
-          const float other = shfl_xor(x, 8);
-          if (m >= p.M || p.tok[m] < 0) continue;
-          float y = x;
-          if (rot) {
-            double sd, cd;
-            sincos(static_cast<double>(p.pos[m]) * inv, &sd, &cd);
-            const float cs = static_cast<float>(cd), sn = static_cast<float>(sd);
-            y = (c < 8) ? (x * cs - other * sn) : (x * cs + other * sn);
-          }
-          const T v = Elem<T>::from_f(y);
-          if (hh < p.nq) {
-            static_cast<T*>(p.out)[m * p.ldo + col] = v;
-          } else {
-            const int b = m / p.rows_per_seq;
-            const int d = p.dest[m];
-            if (b >= p.batch || d < 0 || d >= p.cap) {
-              if (p.status != nullptr) atomicOr(p.status, 1 << 4);
-              continue;
-            }
-            const bool isk = hh < p.nq + p.nkv;
-            const int kvh = isk ? hh - p.nq : hh - p.nq - p.nkv;
-            const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
-            // K rows [cap, hd]; V stored transposed, [hd, cap]
-            if (isk) static_cast<T*>(p.kc)[(bk * p.cap + d) * p.hd + cin] = v;
-            else static_cast<T*>(p.vc)[(bk * p.hd + cin) * p.cap + d] = v;
-          }
-        }
     }
   }
+}
 
+// ---- split-K: the last workgroup of a tile to arrive sums ---------------
+// Partial tiles are written and read with agent-scope atomic (relaxed)
+// stores and loads, which the memory model maps to accesses coherent at
+// device scope (sc1: written through, read past the XCD's L2), and the
+// stores have completed (vmcnt 0) before the arrival counter moves.  A
+// device-scope release fence would do the same by writing back the whole
+// L2 of the XCD, which costs more than the GEMM.  Returns true in the
+// workgroup that arrived last, with acc holding the sum over splits in
+// split order; ctr is that tile's arrival counter (left at zero).
+template <int MT, int CT>
+__device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT][CT],
+                                            int group, int m0, int split, int* ctr) {
+  __shared__ int last;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int ntiles = p.N / 16;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+    if (tile >= ntiles) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + mt * 16 + 4 * g + j;
+        if (m < p.M)
+          __hip_atomic_store(p.part + (static_cast<int64_t>(split) * p.Mtot + m) * p.N +
+                                 tile * 16 + c,
+                             acc[mt][ct][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == p.S - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return false;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + mt * 16 + 4 * g + j;
+        float sum = 0.f;
+        if (m < p.M && tile < ntiles) {
+          for (int sp = 0; sp < p.S; ++sp)
+            sum += __hip_atomic_load(
+                p.part + (static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c,
+                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        acc[mt][ct][j] = sum;
+      }
+  }
+  return true;
 }
 
 template <typename T, int MT, int CT, int PS>
@@ -402,60 +496,149 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
     }
   }
 
-  // ---- split-K: the last workgroup of a column group to arrive sums ------
-  // Partial tiles are written and read with agent-scope atomic (relaxed)
-  // stores and loads, which the memory model maps to accesses coherent at
-  // device scope (sc1: written through, read past the XCD's L2), and the
-  // stores have completed (vmcnt 0) before the arrival counter moves.  A
-  // device-scope release fence would do the same by writing back the whole
-  // L2 of the XCD, which costs more than the GEMM.
   if (p.S > 1) {
-    __shared__ int last;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int tile = (group * 4 + wave) * CT + ct;
-      if (tile >= ntiles) continue;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + mt * 16 + 4 * g + j;
-          if (m < p.M)
-            __hip_atomic_store(p.part + (static_cast<int64_t>(split) * p.Mtot + m) * p.N +
-                                   tile * 16 + c,
-                               acc[mt][ct][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
-      int* ctr = p.cnt + blockIdx.z * ngroups + group;
-      const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = prev == p.S - 1;
-      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!last) return;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int tile = (group * 4 + wave) * CT + ct;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + mt * 16 + 4 * g + j;
-          float sum = 0.f;
-          if (m < p.M && tile < ntiles) {
-            for (int sp = 0; sp < p.S; ++sp)
-              sum += __hip_atomic_load(
-                  p.part + (static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c,
-                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          acc[mt][ct][j] = sum;
-        }
-    }
+    const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
+    if (!splitk_last<MT, CT>(p, acc, group, m0, split, p.cnt + blockIdx.z * ngroups + group))
+      return;
   }
+  epilogue<T, MT, CT>(p, acc, lds, group, m0);
+}
+
+// ============================================================================
+// Dense path: more than 64 rows (a batch of trees) makes the product a dense
+// contraction, bound by the matrix cores.  A is normalised and split into
+// bf16 hi/lo fragments once per launch (pack_a_kernel); then each workgroup
+// computes a 64-row x 256-column tile: its four waves share the A tile,
+// double-buffered in LDS one 128-wide k step at a time, and each wave reads
+// its own 64 columns of packed weights straight into registers, the next
+// step's fragments loaded as the current ones retire.  Workgroups that share
+// a column block are numbered so that they land on the same XCD (dispatch
+// goes round-robin over the 8 XCDs) and reuse its L2 copy of the weights.
+// ============================================================================
+constexpr int kPackASteps = 4;           // k steps of A per pack_a workgroup
+constexpr int kDenseABytes = 16 * kBlk;  // A bytes of one step of a 64-row block
+
+template <typename T>
+__global__ __launch_bounds__(256) void pack_a_kernel(GemmParams p) {
+  __shared__ float rn[64];
+  const int m0 = blockIdx.x * 64;
+  row_factors<4>(p, rn, m0);
+  __syncthreads();
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int s0 = blockIdx.y * kPackASteps;
+  const int k8n = min(kPackASteps, ksteps - s0) * 16;
+  unsigned char* out = static_cast<unsigned char*>(p.apack);
+  for (int idx = threadIdx.x; idx < 64 * k8n; idx += 256) {
+    const int m = idx / k8n, k8 = idx - m * k8n;
+    float v[8];
+    a_values<T>(p, rn, m, m0 + m, (s0 * 16 + k8) * 8, p.K, v);
+    const int s = s0 + (k8 >> 4), rem = k8 & 15;
+    const int g = rem >> 2, e = rem & 3;
+    const int rt = (m0 >> 4) + (m >> 4), c = m & 15;
+    unsigned char* blk = out + ((static_cast<int64_t>(rt) * ksteps + s) * 4 + e) * kBlk;
+    u32x4 hi, lo;
+    split_hi_lo(v, hi, lo);
+    *reinterpret_cast<u32x4*>(blk + (g * 16 + c) * 16) = hi;
+    *reinterpret_cast<u32x4*>(blk + 1024 + (g * 16 + c) * 16) = lo;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dense_gemm_kernel(GemmParams p) {
+  constexpr int MT = 4, CT = 4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ntiles = p.N / 16;
+  const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
+  const int RB = (p.M + 63) / 64;
+  const int ntask = RB * ngroups * p.S;
+  const int per_xcd = (ntask + 7) / 8;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= ntask) return;
+  const int rb = t % RB;
+  const int split = (t / RB) % p.S;
+  const int group = t / (RB * p.S);
+  const int m0 = rb * 64;
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int st0 = split * (p.KS / kStep);
+  const int nsteps = min(p.KS / kStep, ksteps - st0);
+
+  const T* wtile[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tile = (group * 4 + wave) * CT + ct;
+    wtile[ct] = static_cast<const T*>(p.wpack) +
+                static_cast<int64_t>(tile < ntiles ? tile : 0) * 4 * kPackBlk + lane * 8;
+  }
+  const int64_t step_stride = static_cast<int64_t>(ntiles) * 4 * kPackBlk;
+  // the block's four row tiles lie ksteps * 8 KB apart in the packed A
+  const unsigned char* abase = static_cast<const unsigned char*>(p.apack) +
+                               static_cast<int64_t>(rb) * 4 * ksteps * (4 * kBlk);
+  u32x4 ar[8];
+  auto load_a = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = (i * 256 + static_cast<int>(threadIdx.x)) * 16;
+      const int rt = o >> 13, w = o & 8191;
+      ar[i] = *reinterpret_cast<const u32x4*>(
+          abase + (static_cast<int64_t>(rt) * ksteps + st) * (4 * kBlk) + w);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = (i * 256 + static_cast<int>(threadIdx.x)) * 16;
+      const int rt = o >> 13, w = o & 8191;
+      const int e = w >> 11, inb = w & 2047;
+      *reinterpret_cast<u32x4*>(lds + buf * kDenseABytes + ((e * 4 + rt) << 11) + inb) = ar[i];
+    }
+  };
+
+  Frag8<T> wb[CT][4];
+  load_a(st0);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wb[ct][e].load(wtile[ct] + st0 * step_stride + e * kPackBlk);
+  f32x4 acc[MT][CT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  store_a(0);
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    const int nst = st0 + (more ? s + 1 : s);
+    if (more) load_a(nst);
+    const unsigned char* ab = lds + (s & 1) * kDenseABytes;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Frag8<uint16_t> ah, al;
+        ah.v = *reinterpret_cast<const u32x4*>(ab + ((e * 4 + mt) << 11) + lane * 16);
+        al.v = *reinterpret_cast<const u32x4*>(ab + ((e * 4 + mt) << 11) + 1024 + lane * 16);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[mt][ct] = mfma16(ah, wb[ct][e], acc[mt][ct]);
+          acc[mt][ct] = mfma16(al, wb[ct][e], acc[mt][ct]);
+        }
+      }
+      // the next step's fragments of sub-step e replace the retired ones
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) wb[ct][e].load(wtile[ct] + nst * step_stride + e * kPackBlk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) store_a((s + 1) & 1);
+    __syncthreads();
+  }
+
+  if (p.S > 1 && !splitk_last<MT, CT>(p, acc, group, m0, split, p.cnt + rb * ngroups + group))
+    return;
   epilogue<T, MT, CT>(p, acc, lds, group, m0);
 }
 
@@ -504,6 +687,23 @@ int max_piece(int MT) { return MT == 1 ? 8 : 4; }
 
 void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int ntiles = p.N / 16;
+  p.dense = !fp32 && p.M > 64 && p.apack != nullptr && p.M <= p.apack_rows;
+  if (p.dense) {
+    // 64 x 256 tiles; split K until about 1.5 tiles per CU, each split
+    // keeping at least four steps, within the partial-sum buffer
+    const int RB = (p.M + 63) / 64, ngroups = (ntiles + 15) / 16;
+    const int ksteps = (p.K + kStep - 1) / kStep;
+    int S = 1;
+    while (RB * ngroups * S < (3 * num_cus) / 2 && ksteps / (S + 1) >= 4 &&
+           static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
+      ++S;
+    const int steps = (ksteps + S - 1) / S;
+    p.MT = 4; p.CT = 4;
+    p.KS = steps * kStep;
+    p.S = (ksteps + steps - 1) / steps;
+    p.piece_steps = 2;
+    return;
+  }
   const int rows = p.M < 64 ? p.M : 64;
   p.MT = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   const int chunks = (p.M + 16 * p.MT - 1) / (16 * p.MT);
@@ -573,7 +773,42 @@ hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 template <typename T>
+hipError_t launch_dense(const GemmParams& p, hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    const int RB = (p.M + 63) / 64;
+    const int ksteps = (p.K + kStep - 1) / kStep;
+    hipLaunchKernelGGL(pack_a_kernel<T>, dim3(RB, (ksteps + kPackASteps - 1) / kPackASteps),
+                       dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ngroups = (p.N / 16 + 15) / 16;
+    const int ntask = RB * ngroups * p.S;
+    auto kern = dense_gemm_kernel<T>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kDenseABytes);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((ntask + 7) / 8 * 8), dim3(256), 2 * kDenseABytes, s, p);
+    return hipGetLastError();
+  }
+}
+
+template <typename T>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  if (p.dense) {
+    if (p.N % 16 || p.K % 8 || p.K < 8 || p.KS % kStep || p.S < 1 || p.MT != 4 ||
+        p.CT != 4 || static_cast<int64_t>(p.S) * p.KS < p.K || p.M > p.apack_rows ||
+        (p.S > 1 && (p.part == nullptr || p.cnt == nullptr ||
+                     static_cast<int64_t>(p.S) * p.Mtot * p.N > p.part_elems)) ||
+        p.wpack == nullptr || p.apack == nullptr)
+      return hipErrorInvalidValue;
+    return launch_dense<T>(p, s);
+  }
   if (p.N % 16 || p.K % 8 || p.K < 8 || p.KS % kStep || p.S < 1 ||
       static_cast<int64_t>(p.S) * p.KS < p.K ||
       (p.S > 1 && (p.part == nullptr || p.cnt == nullptr)) ||

@@ -48,6 +48,11 @@ struct GemmParams {
   float* part = nullptr;          // [S, Mtot, N] split-K partials
   int64_t part_elems = 0;         // capacity of part (floats)
   int* cnt = nullptr;             // per (row chunk, column group) arrival counters (zero)
+  // dense path (more than 64 rows): A staged once per launch as bf16 hi/lo
+  // fragments, [rows/16][k steps][4][2 KB]; apack_rows rows fit
+  void* apack = nullptr;
+  int apack_rows = 0;
+  int dense = 0;                  // set by plan_gemm
   int epi = EPI_STORE;
   void* out = nullptr;            // float activations (q: weight type)
   int64_t ldo = 0;

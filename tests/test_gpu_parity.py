@@ -25,6 +25,9 @@ CASES = {
     "mid_fp32": lambda: synth.config("tiny", H=512, n_q=8, n_kv=2, F=1376,
                                      V=2000, ctx=(90, 300), D=4, K=5, N=16,
                                      B=2),
+    # batch 23 x 6 rows per sequence = 138 rows: the dense (MFMA-bound) GEMM
+    # path, three 64-row blocks with a ragged last one, split K
+    "mid_b23": lambda: synth.config("8b_bs1", **dict(MID, B=23, s_max=6)),
 }
 
 _models = {}
@@ -42,7 +45,7 @@ def _close(cfg, got, want, what=""):
     np.testing.assert_allclose(got, want, atol=atol, rtol=rtol, err_msg=what)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32", "mid_b23"])
 @pytest.mark.parametrize("rows", [1, 7, 64, 131])
 def test_fuse_parity(name, rows):
     m = model_for(name)
@@ -56,7 +59,7 @@ def test_fuse_parity(name, rows):
     _close(cfg, as_np(g), want, "g")
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32", "mid_b23"])
 def test_draft_step_parity(name):
     """One draft step over causal seed rows of several sequences."""
     m = model_for(name)
@@ -138,12 +141,12 @@ def _run_tree_case(name, check_kv=True):
     return m, seqs, d, kv, tree
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_fp32", "mid_b23"])
 def test_draft_tree_parity(name):
     _run_tree_case(name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_b23"])
 def test_verify_greedy_parity_with_commit(name):
     m, seqs, d, kv, tree = _run_tree_case(name, check_kv=False)
     cfg = m.cfg

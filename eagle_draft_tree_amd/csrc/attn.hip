@@ -273,31 +273,59 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
 }
 
 // Merge of the splits: one workgroup per (query vector, kv head, sequence),
-// one thread per dim; splits are combined in order (deterministic).
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
+// one thread per dim.  The splits' (max, sum) pairs are read by one thread
+// each and reduced across the workgroup, so their loads overlap instead of
+// waiting on each other; the per-split weights go through LDS and every
+// thread then sums its dim over the splits in split order (deterministic).
+constexpr int kMergeThreads = 128;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p) {
+  __shared__ float w_s[kMergeThreads];
+  __shared__ float red_m[kMergeThreads / 64], red_l[kMergeThreads / 64];
   const int m = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
   const int row = b * p.rows_per_seq + m / G;
   if (m >= QG || p.tok[row] < 0) return;
-  const int NSP = p.nsplit + 1;
+  const int NSP = p.nsplit + 1;   // <= kMergeThreads (checked at launch)
   const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
-  float M = -INFINITY;
-  for (int sp = 0; sp < NSP; ++sp) M = fmaxf(M, p.part_ml[((bk * NSP + sp) * QG + m) * 2]);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ms = -INFINITY, ls = 0.f;
+  if (tid < NSP) {
+    const int64_t base = (bk * NSP + tid) * QG + m;
+    ms = p.part_ml[base * 2];
+    ls = p.part_ml[base * 2 + 1];
+  }
+  float M = wave_max(ms);
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red_m[w]);
+  const float wt = (ms == -INFINITY || M == -INFINITY) ? 0.f : expf(ms - M);
+  w_s[tid] = wt;
+  const float L = wave_sum(wt * ls);
+  if (lane == 0) red_l[wave] = L;
+  __syncthreads();
+  float Ltot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) Ltot += red_l[w];
   const int head = kvh * G + m % G;
-  for (int d = threadIdx.x; d < p.hd; d += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int sp = 0; sp < NSP; ++sp) {
-        const int64_t base = (bk * NSP + sp) * QG + m;
-        const float ms = p.part_ml[base * 2];
-        if (ms == -INFINITY) continue;
-        const float w = expf(ms - M);
-        L += w * p.part_ml[base * 2 + 1];
-        O += w * p.part_o[base * p.hd + d];
-      }
+  for (int d = tid; d < p.hd; d += kMergeThreads) {
+    float O = 0.f;
+    const float* po = p.part_o + ((bk * NSP) * QG + m) * p.hd + d;
+    const int64_t stride = static_cast<int64_t>(QG) * p.hd;
+    int sp = 0;
+    for (; sp + 4 <= NSP; sp += 4) {
+      const float o0 = po[(sp + 0) * stride], o1 = po[(sp + 1) * stride];
+      const float o2 = po[(sp + 2) * stride], o3 = po[(sp + 3) * stride];
+      O += w_s[sp] * o0;
+      O += w_s[sp + 1] * o1;
+      O += w_s[sp + 2] * o2;
+      O += w_s[sp + 3] * o3;
     }
-    p.o[(static_cast<int64_t>(row) * p.nq + head) * p.hd + d] = L > 0.f ? O / L : 0.f;
+    for (; sp < NSP; ++sp) O += w_s[sp] * po[sp * stride];
+    p.o[(static_cast<int64_t>(row) * p.nq + head) * p.hd + d] = Ltot > 0.f ? O / Ltot : 0.f;
   }
 }
 
@@ -305,7 +333,8 @@ template <typename T>
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
-  if (QG > 128 || p.split_keys % 64 || p.split_keys < 64) return hipErrorInvalidValue;
+  if (QG > 128 || p.split_keys % 64 || p.split_keys < 64 || p.nsplit + 1 > kMergeThreads)
+    return hipErrorInvalidValue;
   const int nqb = (QG + 15) / 16;
   const int nqg = (nqb + QBW - 1) / QBW;
   const int items = (p.nsplit + 1) * nqg;
@@ -322,7 +351,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(QG, p.nkv, p.batch), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(QG, p.nkv, p.batch), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -13,55 +13,44 @@ constexpr int kMaxPath = 72;            // >= D + 1 when (D-1)K <= 64
 // ============================================================================
 // merge: per row, top-k over the LM-head tiles' candidates + log-sum-exp
 // ============================================================================
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  __shared__ float sv[4 * kMaxTopK];
-  __shared__ int si[4 * kMaxTopK];
-  __shared__ float sm[256], ss[256];
-  const int row = blockIdx.x;
-  if (p.tok[row] < 0) return;
+// Each 64-column tile of the LM head left its top-k (sorted best-first) and
+// (max, sum of exp).  The row's top-k is found from few of them: with theta
+// the k-th largest tile maximum, k tiles hold an element >= theta, so every
+// element of the row's top-k is >= theta and sits in a tile whose maximum is
+// >= theta, within that tile's own top-k.  Those survivors (a few dozen) are
+// sorted by one wave.  If more than kSurv survive (massive ties), every
+// candidate is scanned instead.
+constexpr int kSurv = 64;
+
+// Thread-local sorted top-K of this thread's share of all candidates, then
+// a merge across the workgroup; lane i of wave 0 ends with the i-th best.
+__device__ void merge_all_candidates(const MergeParams& p, int row, float* sv, int* si,
+                                     float& v_out, int& id_out) {
   const int K = p.topk;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int64_t base = static_cast<int64_t>(row) * p.ntile;
-
-  // thread-local sorted top-K
   float lv[kMaxTopK];
   int li[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
   const int ncand = p.ntile * K;
-  // candidates are fetched in batches of 8 per thread so their loads overlap
-  // (one at a time, each waits a full memory latency)
-  constexpr int kBatch = 8;
-  for (int b0 = threadIdx.x; b0 < ncand; b0 += 256 * kBatch) {
-    float bv[kBatch];
-    int bi[kBatch];
+  for (int idx = threadIdx.x; idx < ncand; idx += 256) {
+    const float v = p.cand_val[base * K + idx];
+    const int id = p.cand_id[base * K + idx];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = b0 + u * 256;
-      bv[u] = idx < ncand ? p.cand_val[base * K + idx] : -INFINITY;
-      bi[u] = idx < ncand ? p.cand_id[base * K + idx] : 0x7fffffff;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float v = bv[u];
-      const int id = bi[u];
-      if (!better(v, id, lv[K - 1], li[K - 1])) continue;
-#pragma unroll
-      for (int j = kMaxTopK - 1; j >= 0; --j) {
-        if (j >= K) continue;
-        if (better(v, id, lv[j], li[j])) {
-          if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
-            lv[j] = lv[j - 1];
-            li[j] = li[j - 1];
-          } else {
-            lv[j] = v;
-            li[j] = id;
-          }
+    for (int j = kMaxTopK - 1; j >= 0; --j) {
+      if (j >= K) continue;
+      if (better(v, id, lv[j], li[j])) {
+        if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
+          lv[j] = lv[j - 1];
+          li[j] = li[j - 1];
+        } else {
+          lv[j] = v;
+          li[j] = id;
         }
       }
     }
   }
-  // wave merge: K rounds of "pop the best head"
   for (int r = 0; r < K; ++r) {
     float bv = lv[0];
     int bi = li[0];
@@ -79,51 +68,126 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     }
     if (lane == 0) { sv[wave * K + r] = bv; si[wave * K + r] = bi; }
   }
-  // log-sum-exp over tile statistics
+  __syncthreads();
+  v_out = lane < 4 * K ? sv[lane] : -INFINITY;
+  id_out = lane < 4 * K ? si[lane] : 0x7fffffff;
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  __shared__ float sv[kSurv];
+  __shared__ int si[kSurv];
+  __shared__ float red_a[4], red_b[4];
+  __shared__ int nsurv;
+  const int row = blockIdx.x;
+  if (p.tok[row] < 0) return;
+  const int K = p.topk;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int64_t base = static_cast<int64_t>(row) * p.ntile;
+  if (threadIdx.x == 0) nsurv = 0;
+
+  // ---- tile statistics: log-sum-exp, and this thread's tile maxima ----
+  constexpr int kTPT = 8;   // tile maxima per thread in registers
+  const bool fast = p.ntile <= 256 * kTPT;
+  float hmax[kTPT];
   float M = -INFINITY, S = 0.f;
-  for (int t0 = threadIdx.x; t0 < p.ntile; t0 += 256 * 4) {
-    float mxs[4], ses[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = t0 + u * 256;
-      mxs[u] = t < p.ntile ? p.stat[(base + t) * 2] : -INFINITY;
-      ses[u] = t < p.ntile ? p.stat[(base + t) * 2 + 1] : 0.f;
+  for (int u = 0; u < kTPT; ++u) {
+    const int t = threadIdx.x + 256 * u;
+    hmax[u] = -INFINITY;
+    if (t >= p.ntile) continue;
+    const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
+    hmax[u] = mx;
+    if (mx == -INFINITY) continue;
+    const float nm = fmaxf(M, mx);
+    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
+    M = nm;
+  }
+  for (int t = threadIdx.x + 256 * kTPT; t < p.ntile; t += 256) {
+    const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
+    if (mx == -INFINITY) continue;
+    const float nm = fmaxf(M, mx);
+    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
+    M = nm;
+  }
+  {
+    const float wm = wave_max(M);
+    float ws = wave_sum(M == -INFINITY ? 0.f : S * expf(M - wm));
+    if (wm == -INFINITY) ws = 0.f;
+    if (lane == 0) { red_a[wave] = wm; red_b[wave] = ws; }
+  }
+  // ---- theta: the K-th largest tile maximum.  Each wave takes its K
+  // largest (K rounds: the wave maximum, given up by the lowest lane holding
+  // it), then one wave sorts the four lists ----
+  unsigned taken = 0;
+  for (int r = 0; r < K; ++r) {
+    float mine = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u)
+      if (!((taken >> u) & 1u)) mine = fmaxf(mine, hmax[u]);
+    const float m1 = wave_max(mine);
+    const uint64_t own = __ballot(mine == m1);
+    if (lane == __ffsll(static_cast<long long>(own)) - 1) {
+      bool done = false;
+#pragma unroll
+      for (int u = 0; u < kTPT; ++u)
+        if (!done && !((taken >> u) & 1u) && hmax[u] == m1) {
+          taken |= 1u << u;
+          done = true;
+        }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float mx = mxs[u], se = ses[u];
-      if (mx == -INFINITY) continue;
-      const float nm = fmaxf(M, mx);
-      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
-      M = nm;
+    if (lane == 0) sv[wave * K + r] = m1;
+  }
+  __syncthreads();
+  float theta;
+  {
+    float v = lane < 4 * K ? sv[lane] : -INFINITY;
+    int id = lane;
+    wave_sort_desc(v, id);
+    theta = __shfl(v, K - 1, 64);
+  }
+  if (!fast) theta = -INFINITY;
+  __syncthreads();
+  // ---- survivors: candidates >= theta of tiles whose maximum is >= theta ----
+  for (int t = threadIdx.x; t < p.ntile; t += 256) {
+    const float mx = p.stat[(base + t) * 2];
+    if (theta == -INFINITY || !(mx >= theta)) continue;
+    for (int j = 0; j < K; ++j) {
+      const float v = p.cand_val[(base + t) * K + j];
+      if (!(v >= theta)) break;
+      const int slot = atomicAdd(&nsurv, 1);
+      if (slot < kSurv) {
+        sv[slot] = v;
+        si[slot] = p.cand_id[(base + t) * K + j];
+      }
     }
   }
-  sm[threadIdx.x] = M;
-  ss[threadIdx.x] = S;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
-      const float m1 = sm[threadIdx.x], m2 = sm[threadIdx.x + w];
-      const float s1 = ss[threadIdx.x], s2 = ss[threadIdx.x + w];
-      const float nm = fmaxf(m1, m2);
-      float s = 0.f;
-      if (nm != -INFINITY)
-        s = (m1 == -INFINITY ? 0.f : s1 * expf(m1 - nm)) +
-            (m2 == -INFINITY ? 0.f : s2 * expf(m2 - nm));
-      sm[threadIdx.x] = nm;
-      ss[threadIdx.x] = s;
-    }
+  const int n = nsurv;
+  float v;
+  int id;
+  if (n <= kSurv && theta != -INFINITY) {
+    v = lane < n ? sv[lane] : -INFINITY;
+    id = lane < n ? si[lane] : 0x7fffffff;
+  } else {
     __syncthreads();
+    merge_all_candidates(p, row, sv, si, v, id);
   }
   if (wave == 0) {
-    float v = lane < 4 * K ? sv[lane] : -INFINITY;
-    int id = lane < 4 * K ? si[lane] : 0x7fffffff;
     wave_sort_desc(v, id);
     if (lane < K) {
       p.out_id[static_cast<int64_t>(row) * K + lane] = id;
       p.out_val[static_cast<int64_t>(row) * K + lane] = v;
     }
-    if (lane == 0) p.out_lse[row] = sm[0] + logf(ss[0]);
+    if (lane == 0) {
+      float Mt = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, red_a[w]);
+      float St = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (red_a[w] != -INFINITY) St += red_b[w] * expf(red_a[w] - Mt);
+      p.out_lse[row] = Mt + logf(St);
+    }
   }
 }
 

@@ -53,6 +53,7 @@ __all__ = [
     "LOG_EPS", "bf16_round", "store", "Weights", "rmsnorm", "rope", "silu",
     "fuse", "layer", "topk_desc", "lse32", "child_logprob", "DraftKV",
     "draft_tree", "select_key", "eagle2_tree", "flatten", "verify", "verify_row",
+    "block", "tree_ancestors", "target_tree_layer",
     "commit", "decision_margin", "score_rows", "causal_attention", "attend",
     "philox4x64", "philox4x64_np", "uniform01", "verify_uniforms",
     "STREAM_VERIFY", "STREAM_DRAFT", "BONUS_DRAW",
@@ -199,16 +200,26 @@ def layer(W: Weights, kv: DraftKV, src, tok, pos, dest, visible):
 
     Returns dict with x, q, k, v, o, h, t, a (stored values) and fp32 logits.
     """
+    src = np.atleast_2d(np.asarray(src, dtype=np.float64))
+    tok = np.asarray(tok, dtype=np.int64)
+    x = store(np.concatenate([src, W.embed[tok]], axis=1) @ W.w_in.T, "fp32")
+    return block(W, kv, x, pos, dest, visible)
+
+
+def block(W: Weights, kv: DraftKV, x, pos, dest, visible):
+    """The decoder block after the input: pre-norm attention with RoPE and
+    GQA over the visible cache rows, residual, pre-norm SwiGLU, residual,
+    then the final norm and the LM head ([E3] 6 "Limitation 6": the LLaMA
+    block).  x [R,H] is the block input; every row's K/V is written to the
+    cache before any row attends.  Returns dict with x, q, k, v, o, h, t, a
+    (stored values) and fp32 logits."""
     cfg = W.cfg
     dt, eps = cfg.dtype, cfg.eps
     f32 = "fp32"
-    src = np.atleast_2d(np.asarray(src, dtype=np.float64))
-    tok = np.asarray(tok, dtype=np.int64)
-    R = src.shape[0]
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    R = x.shape[0]
     nq, nkv, hd = cfg.n_q, cfg.n_kv, cfg.hd
     group = nq // nkv
-
-    x = store(np.concatenate([src, W.embed[tok]], axis=1) @ W.w_in.T, f32)
     n1 = rmsnorm(x, W.g_attn, eps, f32)
     q = rope((n1 @ W.wq.T).reshape(R, nq, hd), pos, cfg.theta)
     k = rope((n1 @ W.wk.T).reshape(R, nkv, hd), pos, cfg.theta)
@@ -482,6 +493,39 @@ def score_rows(W: Weights, kv: DraftKV, tree, info):
         for i, (r, _) in enumerate(todo):
             out[r] = o["logits"][i]
     return out
+
+
+# ---------------------------------------------------------------------------
+# the target's verification forward over the flattened tree
+# ---------------------------------------------------------------------------
+def tree_ancestors(tree, r: int) -> list:
+    """Flattened rows on the path from the root to row r, r included."""
+    out = []
+    while r >= 0:
+        out.append(int(r))
+        r = int(tree["parent"][r])
+    return out[::-1]
+
+
+def target_tree_layer(W: Weights, kv: DraftKV, tree, len_in: int):
+    """One target decoder layer over the N+1 flattened tree rows in a single
+    pass under tree attention ([E1] "The Full Inference Loop", Phase 2: the
+    target processes the prompt plus the draft tree in one forward pass;
+    [E3] 3.4 "The Inference Pipeline", Stage 2; [M75] 0x05C).  Row r takes
+    the embedding of its token as input, rotates at its tree position,
+    writes its K/V to cache row len_in + r, and sees the committed prefix
+    [0, len_in) plus the rows of its own root-to-r path.  Returns the block
+    outputs of rows 0..n_nodes: a [n+1, H] and float32 logits [n+1, V]
+    (the target's next-token logits after each row)."""
+    n = int(tree["n_nodes"])
+    rows = list(range(n + 1))
+    tok = np.asarray([tree["token"][r] for r in rows], dtype=np.int64)
+    x = store(W.embed[tok], "fp32")
+    vis = [np.concatenate([np.arange(len_in, dtype=np.int64),
+                           len_in + np.asarray(tree_ancestors(tree, r), dtype=np.int64)])
+           for r in rows]
+    return block(W, kv, x, pos=np.asarray([tree["position"][r] for r in rows]),
+                 dest=np.asarray([len_in + r for r in rows]), visible=vis)
 
 
 def decision_margin(cfg, tree_info) -> float:

@@ -269,6 +269,34 @@ class Drafter:
         return out
 
 
+    def target_workspace_bytes(self, batch) -> int:
+        n = lib().eagle_target_layer_workspace_bytes(ctypes.byref(self._cfg), int(batch))
+        if n == 0:
+            raise EagleError(2, "eagle_target_layer_workspace_bytes (shape rejected)")
+        return int(n)
+
+    def target_tree_layer(self, tree, kv: KVCache, logits=None, hidden=None,
+                          workspace=None):
+        """The target's one-pass forward over the flattened trees (this
+        context's weights are the target layer's).  Returns (logits
+        [B, N+1, V] fp32, hidden [B, N+1, H] fp32 or None)."""
+        B = tree["token"].shape[0]
+        N1 = self.shape.budget + 1
+        dev = tree["token"].device
+        if logits is None:
+            logits = torch.empty(B, N1, self.shape.vocab, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(self.target_workspace_bytes(B), dtype=torch.uint8,
+                                    device=dev)
+        ckv = kv.c_kv(kv.length, None)
+        ct = self._c_tree(tree)
+        check(lib().eagle_target_tree_layer(
+            self._ctx, B, ctypes.byref(ct), ctypes.byref(ckv), _ptr(workspace),
+            workspace.numel(), None if hidden is None else _ptr(hidden), _ptr(logits),
+            _stream()), "eagle_target_tree_layer")
+        return logits, hidden
+
+
 def draw_uniforms(seed, stream_id, round, batch, rows, draws, device="cuda"):
     """U[0,1) draws [batch, rows, draws] of the library's Philox generator."""
     out = torch.empty(batch, rows, draws, dtype=torch.float32, device=device)

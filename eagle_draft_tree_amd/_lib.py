@@ -15,7 +15,8 @@ EXPORTS = ("eagle_workspace_bytes", "eagle_create", "eagle_destroy",
            "eagle_status_str", "eagle_get_device_status", "eagle_fuse_features",
            "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree",
            "eagle_verify_tree_uniforms", "eagle_verify_tree_noalloc",
-           "eagle_draw_uniforms",
+           "eagle_draw_uniforms", "eagle_target_layer_workspace_bytes",
+           "eagle_target_tree_layer",
            "eagle_profile", "eagle_profile_read")
 COMMIT_KEEP, COMMIT_RESEED = 0, 1
 STREAM_VERIFY, STREAM_DRAFT = 0, 1
@@ -112,6 +113,11 @@ def lib():
     L.eagle_draw_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
                                       ctypes.c_uint64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, vp, vp]
+    L.eagle_target_layer_workspace_bytes.restype = ctypes.c_size_t
+    L.eagle_target_layer_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32]
+    L.eagle_target_tree_layer.restype = ctypes.c_int
+    L.eagle_target_tree_layer.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Tree),
+                                          ctypes.POINTER(KV), vp, ctypes.c_size_t, vp, vp, vp]
     L.eagle_profile.restype = ctypes.c_int
     L.eagle_profile.argtypes = [vp, ctypes.c_int32]
     L.eagle_profile_read.restype = ctypes.c_int

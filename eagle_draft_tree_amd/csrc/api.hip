@@ -211,6 +211,39 @@ struct eagle_ctx {
 
 namespace {
 
+// Activation, partial-sum and candidate buffers of one layer pass: the
+// context's workspace for draft passes, the caller's for the target layer.
+struct Scratch {
+  char *x = nullptr, *h = nullptr, *o = nullptr, *t = nullptr, *q = nullptr;
+  float* ss = nullptr;
+  float* part = nullptr;
+  int64_t part_elems = 0;
+  int* cnt = nullptr;
+  char* apack = nullptr;
+  int apack_rows = 0;
+  float *at_o = nullptr, *at_ml = nullptr;
+  int max_split = 1;
+  float* lm_val = nullptr;
+  int32_t* lm_id = nullptr;
+  float* lm_stat = nullptr;
+  int ntile_lm = 0;
+};
+
+Scratch ctx_scratch(eagle_ctx* c) {
+  const Offsets& f = c->off;
+  Scratch r;
+  r.x = c->at<char>(f.x); r.h = c->at<char>(f.h); r.o = c->at<char>(f.o);
+  r.t = c->at<char>(f.t); r.q = c->at<char>(f.q); r.ss = c->at<float>(f.ss);
+  r.part = c->at<float>(f.part); r.part_elems = f.part_elems;
+  r.cnt = c->at<int>(f.cnt_gemm);
+  r.apack = f.apack_rows > 0 ? c->at<char>(f.apack) : nullptr;
+  r.apack_rows = f.apack_rows;
+  r.at_o = c->at<float>(f.at_o); r.at_ml = c->at<float>(f.at_ml); r.max_split = f.max_split;
+  r.lm_val = c->at<float>(f.lm_val); r.lm_id = c->at<int32_t>(f.lm_id);
+  r.lm_stat = c->at<float>(f.lm_stat); r.ntile_lm = f.ntile_lm;
+  return r;
+}
+
 // kernel classes reported by eagle_profile_read
 enum ProfClass { PC_GEMM = 0, PC_FUSE = 1, PC_ATTN = 2, PC_MERGE = 3, PC_TREE = 4,
                  PC_VERIFY = 5, PC_COUNT = 6 };
@@ -248,17 +281,18 @@ struct Rows {  // one pass's query rows
 };
 
 template <typename T>
-hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEMM) {
+hipError_t run_gemm(eagle_ctx* c, const Scratch& scr, GemmParams& p, hipStream_t s,
+                    int cls = PC_GEMM) {
   double a_bytes = 0;
   for (int i = 0; i < p.nseg; ++i)
     a_bytes += static_cast<double>(p.M) * p.seg[i].width * (p.seg[i].f32 ? 4 : sizeof(T));
   p.Mtot = (p.M + 15) / 16 * 16;
-  p.part = c->at<float>(c->off.part);
-  p.part_elems = c->off.part_elems;
-  p.cnt = c->at<int>(c->off.cnt_gemm);
+  p.part = scr.part;
+  p.part_elems = scr.part_elems;
+  p.cnt = scr.cnt;
   p.eps = c->cfg.rms_eps;
-  p.apack = c->off.apack_rows > 0 ? c->at<char>(c->off.apack) : nullptr;
-  p.apack_rows = c->off.apack_rows;
+  p.apack = scr.apack;
+  p.apack_rows = scr.apack_rows;
   plan_gemm(p, c->num_cus, sizeof(T) == 4);
   // algorithmic bytes: weights once, activation rows in, results out
   const double w_bytes = static_cast<double>(p.N) * p.K * sizeof(T);
@@ -270,55 +304,45 @@ hipError_t run_gemm(eagle_ctx* c, GemmParams& p, hipStream_t s, int cls = PC_GEM
   return e;
 }
 
+#define EAGLE_TRY(x)                        \
+  do {                                      \
+    if ((x) != hipSuccess) return EAGLE_EHIP; \
+  } while (0)
+
+// One decoder block over rows r whose input x already sits in scr.x (with
+// its per-16-column sums of squares in scr.ss): RMSNorm -> QKV -> RoPE ->
+// cache rows, tree attention, O-projection + residual, RMSNorm -> SwiGLU ->
+// down + residual into a_out, then the final norm and the LM head: per-row
+// top-k and log-sum-exp into r.topk_* / r.lse, or (logits != null) every
+// logit, fp32 [rows, V].
 template <typename T>
-eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
-                       hipStream_t s) {
+eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const eagle_kv* kv,
+                       void* a_out, float* logits, hipStream_t s) {
   const eagle_config& cf = c->cfg;
-  const Offsets& f = c->off;
   const int H = cf.hidden, F = cf.ffn;
   const int qd = cf.n_q_heads * cf.head_dim;
   const int R = r.batch * r.rps;
-  hipError_t e;
-#define EAGLE_TRY(x)                 \
-  do {                               \
-    e = (x);                         \
-    if (e != hipSuccess) return EAGLE_EHIP; \
-  } while (0)
-
-  // a2 join: x = W_I [src ; E[tok]]
-  {
-    GemmParams p;
-    c->shape(G_IN, p);
-    p.M = R; p.nseg = 2;
-    p.seg[0].base = r.src; p.seg[0].ld = H; p.seg[0].rowidx = r.src_row;
-    p.seg[0].rowlimit = r.src_rows; p.seg[0].width = H;
-    p.seg[1].base = c->w.embed; p.seg[1].ld = H; p.seg[1].rowidx = r.tok;
-    p.seg[1].rowlimit = tvocab(cf); p.seg[1].width = H; p.seg[1].f32 = 0;
-    p.epi = EPI_STORE; p.out = c->at<char>(f.x); p.ldo = H;
-    p.ss = c->at<float>(f.ss);
-    EAGLE_TRY(run_gemm<T>(c, p, s));
-  }
   // a3 RMSNorm -> QKV -> RoPE -> q buffer + KV cache rows
   {
     GemmParams p;
     c->shape(G_QKV, p);
     p.M = R; p.nseg = 1;
-    p.seg[0].base = c->at<char>(f.x); p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].base = scr.x; p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].ss = scr.ss; p.seg[0].ss_tiles = H / 16;
     p.seg[0].gain = c->w.g_attn;
-    p.epi = EPI_QKV; p.out = c->at<char>(f.q); p.ldo = qd;
+    p.epi = EPI_QKV; p.out = scr.q; p.ldo = qd;
     p.pos = r.pos; p.dest = r.dest; p.tok = r.tok; p.rows_per_seq = r.rps;
     p.kc = kv->k; p.vc = kv->v; p.cap = kv->cap; p.nq = cf.n_q_heads;
     p.nkv = cf.n_kv_heads; p.batch = r.batch; p.theta = cf.rope_theta;
     p.status = c->status();
-    EAGLE_TRY(run_gemm<T>(c, p, s));
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
   }
   // a4 tree attention
   {
     AttnParams p;
     p.batch = r.batch; p.rows_per_seq = r.rps; p.nq = cf.n_q_heads;
     p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.cap = kv->cap;
-    p.q = c->at<char>(f.q); p.o = c->at<float>(f.o);
+    p.q = scr.q; p.o = reinterpret_cast<float*>(scr.o);
     p.kc = kv->k; p.vc = kv->v; p.tok = r.tok; p.plen = r.plen;
     p.sbase = r.sbase; p.smask = r.mask;
     // splits: about 8192 waves over the batch (each keeps only one 32-key
@@ -326,11 +350,11 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     const int G = cf.n_q_heads / cf.n_kv_heads;
     const int nqg = ((r.rps * G + 15) / 16 + 1) / 2;
     const int want = std::max(1, 8192 / std::max(1, r.batch * cf.n_kv_heads * nqg));
-    int nsplit = std::min({f.max_split, std::max(1, (kv->cap + 63) / 64), want});
+    int nsplit = std::min({scr.max_split, std::max(1, (kv->cap + 63) / 64), want});
     const int split_keys = std::max(64, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);
     nsplit = (kv->cap + split_keys - 1) / split_keys;
     p.nsplit = nsplit; p.split_keys = split_keys;
-    p.part_o = c->at<float>(f.at_o); p.part_ml = c->at<float>(f.at_ml);
+    p.part_o = scr.at_o; p.part_ml = scr.at_ml;
     p.scale = 1.0f / sqrtf(static_cast<float>(cf.head_dim));
     const int pi = prof_begin(c, PC_ATTN, 0.0, 0.0, s);
     EAGLE_TRY(launch_attention<T>(p, s));
@@ -341,56 +365,81 @@ eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv,
     GemmParams p;
     c->shape(G_O, p);
     p.M = R; p.nseg = 1;
-    p.seg[0].base = c->at<char>(f.o); p.seg[0].ld = qd; p.seg[0].width = qd;
-    p.epi = EPI_RESID; p.out = c->at<char>(f.h); p.ldo = H;
-    p.resid = c->at<float>(f.x); p.ldr = H;
-    p.ss = c->at<float>(f.ss);
-    EAGLE_TRY(run_gemm<T>(c, p, s));
+    p.seg[0].base = scr.o; p.seg[0].ld = qd; p.seg[0].width = qd;
+    p.epi = EPI_RESID; p.out = scr.h; p.ldo = H;
+    p.resid = reinterpret_cast<const float*>(scr.x); p.ldr = H;
+    p.ss = scr.ss;
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
   }
   // a6 t = silu(Wg n2) * (Wu n2)
   {
     GemmParams p;
     c->shape(G_GU, p);
     p.M = R; p.nseg = 1;
-    p.seg[0].base = c->at<char>(f.h); p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].base = scr.h; p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].ss = scr.ss; p.seg[0].ss_tiles = H / 16;
     p.seg[0].gain = c->w.g_mlp;
-    p.epi = EPI_SWIGLU; p.out = c->at<char>(f.t); p.ldo = F;
-    EAGLE_TRY(run_gemm<T>(c, p, s));
+    p.epi = EPI_SWIGLU; p.out = scr.t; p.ldo = F;
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
   }
   //    a = h + Wd t
   {
     GemmParams p;
     c->shape(G_DOWN, p);
     p.M = R; p.nseg = 1;
-    p.seg[0].base = c->at<char>(f.t); p.seg[0].ld = F; p.seg[0].width = F;
-    p.epi = EPI_RESID; p.out = r.a_out; p.ldo = H;
-    p.resid = c->at<float>(f.h); p.ldr = H;
-    p.ss = c->at<float>(f.ss);
-    EAGLE_TRY(run_gemm<T>(c, p, s));
+    p.seg[0].base = scr.t; p.seg[0].ld = F; p.seg[0].width = F;
+    p.epi = EPI_RESID; p.out = a_out; p.ldo = H;
+    p.resid = reinterpret_cast<const float*>(scr.h); p.ldr = H;
+    p.ss = scr.ss;
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
   }
-  // a7 final norm -> LM head -> per-tile top-k -> merge
+  // a7 final norm -> LM head -> per-tile top-k -> merge (or every logit)
   {
     GemmParams p;
     c->shape(G_LM, p);
     p.M = R; p.nseg = 1;
-    p.seg[0].base = r.a_out; p.seg[0].ld = H; p.seg[0].width = H;
-    p.seg[0].ss = c->at<float>(f.ss); p.seg[0].ss_tiles = H / 16;
+    p.seg[0].base = a_out; p.seg[0].ld = H; p.seg[0].width = H;
+    p.seg[0].ss = scr.ss; p.seg[0].ss_tiles = H / 16;
     p.seg[0].gain = c->w.g_final;
+    if (logits != nullptr) {
+      p.epi = EPI_STORE; p.out = logits; p.ldo = cf.vocab;
+      EAGLE_TRY(run_gemm<T>(c, scr, p, s));
+      return EAGLE_OK;
+    }
     p.epi = EPI_LMHEAD;
-    p.cand_val = c->at<float>(f.lm_val); p.cand_id = c->at<int32_t>(f.lm_id);
-    p.stat = c->at<float>(f.lm_stat); p.ntile_lm = f.ntile_lm; p.topk = cf.topk;
-    EAGLE_TRY(run_gemm<T>(c, p, s));
+    p.cand_val = scr.lm_val; p.cand_id = scr.lm_id;
+    p.stat = scr.lm_stat; p.ntile_lm = scr.ntile_lm; p.topk = cf.topk;
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
     MergeParams m;
-    m.rows = R; m.ntile = f.ntile_lm; m.topk = cf.topk;
+    m.rows = R; m.ntile = scr.ntile_lm; m.topk = cf.topk;
     m.cand_val = p.cand_val; m.cand_id = p.cand_id; m.stat = p.stat;
     m.tok = r.tok; m.out_id = r.topk_id; m.out_val = r.topk_val; m.out_lse = r.lse;
     const int pi = prof_begin(c, PC_MERGE, 0.0, 0.0, s);
     EAGLE_TRY(launch_merge(m, s));
     prof_end(c, pi, s);
   }
-#undef EAGLE_TRY
   return EAGLE_OK;
+}
+
+// One draft pass: a2 join x = W_I [src ; E[tok]], then the block.
+template <typename T>
+eagle_status run_layer(eagle_ctx* c, const Rows& r, const eagle_kv* kv, hipStream_t s) {
+  const eagle_config& cf = c->cfg;
+  const int H = cf.hidden;
+  const Scratch scr = ctx_scratch(c);
+  {
+    GemmParams p;
+    c->shape(G_IN, p);
+    p.M = r.batch * r.rps; p.nseg = 2;
+    p.seg[0].base = r.src; p.seg[0].ld = H; p.seg[0].rowidx = r.src_row;
+    p.seg[0].rowlimit = r.src_rows; p.seg[0].width = H;
+    p.seg[1].base = c->w.embed; p.seg[1].ld = H; p.seg[1].rowidx = r.tok;
+    p.seg[1].rowlimit = tvocab(cf); p.seg[1].width = H; p.seg[1].f32 = 0;
+    p.epi = EPI_STORE; p.out = scr.x; p.ldo = H;
+    p.ss = scr.ss;
+    EAGLE_TRY(run_gemm<T>(c, scr, p, s));
+  }
+  return run_block<T>(c, scr, r, kv, r.a_out, nullptr, s);
 }
 
 QueryDesc desc_of(eagle_ctx* c, int set) {
@@ -477,6 +526,98 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
     prof_end(c, pi, s);
   }
   return EAGLE_OK;
+}
+
+// Workspace of the target tree layer for `batch` sequences of budget + 1
+// flattened rows: the block's activation buffers, split-K partials and
+// counters, the packed A of the dense path, attention partials and the
+// per-row descriptors.
+struct TargetLayout {
+  size_t x, h, a, o, t, ss, q, part, cnt, apack, at_o, at_ml, tok, pos, dest, plen, mask,
+      sbase, total;
+  int R, n1, max_split, apack_rows, ncnt;
+  int64_t part_elems;
+};
+
+TargetLayout target_layout(const eagle_config& c, int batch) {
+  TargetLayout f;
+  Layout L;
+  const int es = esize(c);
+  const int H = c.hidden, F = c.ffn, V = c.vocab;
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  f.n1 = c.budget + 1;
+  f.R = batch * f.n1;
+  const size_t R = static_cast<size_t>((f.R + 63) / 64 * 64);
+  f.x = L.take(R * H * 4);
+  f.h = L.take(R * H * 4);
+  f.a = L.take(R * H * 4);
+  f.o = L.take(R * qd * 4);
+  f.t = L.take(R * F * 4);
+  f.ss = L.take(R * (H / 16) * 4);
+  f.q = L.take(R * qd * es);
+  const int maxN = std::max(std::max(V, 2 * F), std::max(H, qd + 2 * kd));
+  f.part_elems = static_cast<int64_t>(16) * std::min<int64_t>(R, 32) * maxN;
+  f.part = L.take(static_cast<size_t>(f.part_elems) * 4);
+  f.ncnt = static_cast<int>((R / 16 + 1) * (maxN / 64 + 1));
+  f.cnt = L.take(static_cast<size_t>(f.ncnt) * 4);
+  f.apack_rows = (c.dtype == EAGLE_BF16 && f.R > 64) ? static_cast<int>(R) : 0;
+  const int kmax = std::max(std::max(H, qd), F);
+  f.apack = L.take(static_cast<size_t>(f.apack_rows) * ((kmax + 127) / 128 * 128) * 4);
+  // attention partials: as many splits as the draft passes use, within
+  // about 64 MB
+  const int G = c.n_q_heads / c.n_kv_heads;
+  const double per_split = static_cast<double>(batch) * c.n_kv_heads * f.n1 * G *
+                           (c.head_dim + 2) * 4.0;
+  const int cap_split = static_cast<int>(std::max(1.0, (64.0 * (1 << 20)) / per_split - 1.0));
+  f.max_split = std::max(1, std::min(attn_max_split(batch, c.n_kv_heads), cap_split));
+  const size_t bk = static_cast<size_t>(batch) * c.n_kv_heads * (f.max_split + 1) * f.n1 * G;
+  f.at_o = L.take(bk * c.head_dim * 4);
+  f.at_ml = L.take(bk * 2 * 4);
+  f.tok = L.take(R * 4);
+  f.pos = L.take(R * 4);
+  f.dest = L.take(R * 4);
+  f.plen = L.take(R * 4);
+  f.mask = L.take(R * 8);
+  f.sbase = L.take(static_cast<size_t>(batch) * 4);
+  f.total = L.total;
+  return f;
+}
+
+template <typename T>
+eagle_status target_layer_impl(eagle_ctx* c, int batch, const eagle_tree* tree,
+                               const eagle_kv* kv, char* ws, float* hidden_out,
+                               float* logits_out, hipStream_t s) {
+  const eagle_config& cf = c->cfg;
+  const TargetLayout f = target_layout(cf, batch);
+  auto at = [&](size_t o) { return ws + o; };
+  EAGLE_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(at(f.cnt)), 0, f.ncnt, s));
+  TargetRowsParams tp;
+  tp.batch = batch; tp.n1 = f.n1; tp.cap = kv->cap; tp.mask_words = (f.n1 + 63) / 64;
+  tp.len_in = kv->len_in; tp.token = tree->token; tp.position = tree->position;
+  tp.mask = reinterpret_cast<const uint64_t*>(tree->mask); tp.n_nodes = tree->n_nodes;
+  tp.tok = reinterpret_cast<int32_t*>(at(f.tok)); tp.pos = reinterpret_cast<int32_t*>(at(f.pos));
+  tp.dest = reinterpret_cast<int32_t*>(at(f.dest));
+  tp.plen = reinterpret_cast<int32_t*>(at(f.plen));
+  tp.rmask = reinterpret_cast<uint64_t*>(at(f.mask));
+  tp.sbase = reinterpret_cast<int32_t*>(at(f.sbase)); tp.status = c->status();
+  EAGLE_TRY(launch_target_rows(tp, s));
+  EAGLE_TRY(launch_embed_rows<T>(static_cast<const T*>(c->w.embed), tvocab(cf), tp.tok, f.R,
+                                 cf.hidden, reinterpret_cast<float*>(at(f.x)),
+                                 reinterpret_cast<float*>(at(f.ss)), s));
+  Scratch scr;
+  scr.x = at(f.x); scr.h = at(f.h); scr.o = at(f.o); scr.t = at(f.t); scr.q = at(f.q);
+  scr.ss = reinterpret_cast<float*>(at(f.ss));
+  scr.part = reinterpret_cast<float*>(at(f.part)); scr.part_elems = f.part_elems;
+  scr.cnt = reinterpret_cast<int*>(at(f.cnt));
+  scr.apack = f.apack_rows > 0 ? at(f.apack) : nullptr; scr.apack_rows = f.apack_rows;
+  scr.at_o = reinterpret_cast<float*>(at(f.at_o));
+  scr.at_ml = reinterpret_cast<float*>(at(f.at_ml)); scr.max_split = f.max_split;
+  Rows r;
+  r.batch = batch; r.rps = f.n1;
+  r.tok = tp.tok; r.pos = tp.pos; r.dest = tp.dest; r.plen = tp.plen;
+  r.sbase = tp.sbase; r.mask = tp.rmask;
+  void* a_out = hidden_out != nullptr ? static_cast<void*>(hidden_out) : at(f.a);
+  return run_block<T>(c, scr, r, kv, a_out, logits_out, s);
 }
 
 bool null_tree(const eagle_tree* t) {
@@ -613,8 +754,10 @@ eagle_status eagle_fuse_features(eagle_ctx* ctx, int32_t rows, const void* low,
     p.epi = EPI_STORE;
     p.out = static_cast<float*>(g_out) + static_cast<size_t>(r0) * H;
     p.ldo = H;
-    hipError_t e = ctx->cfg.dtype == EAGLE_BF16 ? run_gemm<uint16_t>(ctx, p, stream, PC_FUSE)
-                                                : run_gemm<float>(ctx, p, stream, PC_FUSE);
+    const Scratch scr = ctx_scratch(ctx);
+    hipError_t e = ctx->cfg.dtype == EAGLE_BF16
+                       ? run_gemm<uint16_t>(ctx, scr, p, stream, PC_FUSE)
+                       : run_gemm<float>(ctx, scr, p, stream, PC_FUSE);
     if (e != hipSuccess) return EAGLE_EHIP;
   }
   return EAGLE_OK;
@@ -842,6 +985,34 @@ eagle_status eagle_verify_tree_noalloc(const eagle_config* cfg, int32_t batch,
   return verify_core(*cfg, ws, nullptr, batch, tree, target_logits, temperature, nullptr,
                      seed, round, commit_mode, kv_or_null, accept_len, accepted_rows,
                      out_tokens, next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+size_t eagle_target_layer_workspace_bytes(const eagle_config* cfg, int32_t batch) {
+  if (check_config(cfg) != EAGLE_OK || batch < 1 || batch > cfg->max_batch ||
+      cfg->budget + 1 > 64)
+    return 0;
+  return target_layout(*cfg, batch).total;
+}
+
+eagle_status eagle_target_tree_layer(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                                     const eagle_kv* kv, void* workspace, size_t ws_bytes,
+                                     float* hidden_out, float* logits_out,
+                                     hipStream_t stream) {
+  if (ctx == nullptr || tree == nullptr || kv == nullptr || workspace == nullptr ||
+      logits_out == nullptr)
+    return EAGLE_EINVAL;
+  if (!tree->token || !tree->position || !tree->mask || !tree->n_nodes || !kv->k || !kv->v ||
+      !kv->len_in || kv->cap <= 0)
+    return EAGLE_EINVAL;
+  const eagle_config& cf = ctx->cfg;
+  if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
+  if (cf.budget + 1 > 64) return EAGLE_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return EAGLE_EINVAL;
+  if (ws_bytes < target_layout(cf, batch).total) return EAGLE_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return cf.dtype == EAGLE_BF16
+             ? target_layer_impl<uint16_t>(ctx, batch, tree, kv, ws, hidden_out, logits_out, stream)
+             : target_layer_impl<float>(ctx, batch, tree, kv, ws, hidden_out, logits_out, stream);
 }
 
 eagle_status eagle_draw_uniforms(uint64_t seed, uint64_t stream_id, uint64_t round,

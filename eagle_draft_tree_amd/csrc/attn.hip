@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
   const int row0 = b * p.rows_per_seq;
 
   // keys any row of this sequence may see: lane i reads row i, then a wave
-  // reduction (rows_per_seq <= 16)
+  // reduction (rows_per_seq <= 64)
   int kmax = 0;
   uint64_t umask = 0;
   if (lane < p.rows_per_seq && p.tok[row0 + lane] >= 0) {
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
     umask = p.smask[row0 + lane];
   }
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
+  for (int o = 1; o < 64; o <<= 1) {
     kmax = max(kmax, shfl_xor(kmax, o));
     const uint32_t lo = static_cast<uint32_t>(umask), hi = static_cast<uint32_t>(umask >> 32);
     const uint32_t olo = static_cast<uint32_t>(shfl_xor(static_cast<int>(lo), o));
@@ -333,7 +333,8 @@ template <typename T>
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
-  if (QG > 128 || p.split_keys % 64 || p.split_keys < 64 || p.nsplit + 1 > kMergeThreads)
+  if (p.rows_per_seq > 64 || QG > 1024 || p.split_keys % 64 || p.split_keys < 64 ||
+      p.nsplit + 1 > kMergeThreads)
     return hipErrorInvalidValue;
   const int nqb = (QG + 15) / 16;
   const int nqg = (nqb + QBW - 1) / QBW;

@@ -408,7 +408,6 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
   const int ntiles = p.N / 16;
   const int group = blockIdx.x / p.S;
   const int split = blockIdx.x % p.S;

@@ -178,6 +178,25 @@ struct VerifyParams {
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+// target tree layer: per-row descriptors from the flattened tree, and the
+// block input x = E[token] (fp32) with its per-16-column sums of squares
+struct TargetRowsParams {
+  int batch = 0, n1 = 0, cap = 0, mask_words = 1;
+  const int32_t* len_in = nullptr;     // [B] committed length = first tree cache row
+  const int32_t* token = nullptr;      // tree arrays [B, n1]
+  const int32_t* position = nullptr;
+  const uint64_t* mask = nullptr;      // [B, n1, mask_words]
+  const int32_t* n_nodes = nullptr;    // [B]
+  int32_t *tok = nullptr, *pos = nullptr, *dest = nullptr, *plen = nullptr;  // [B*n1]
+  uint64_t* rmask = nullptr;           // [B*n1]
+  int32_t* sbase = nullptr;            // [B]
+  int* status = nullptr;
+};
+hipError_t launch_target_rows(const TargetRowsParams& p, hipStream_t s);
+template <typename T>
+hipError_t launch_embed_rows(const T* embed, int vocab, const int32_t* tok, int rows, int H,
+                             float* x, float* ss, hipStream_t s);
 hipError_t launch_uniforms(uint64_t seed, uint64_t stream, uint64_t rnd, int batch, int rows,
                            int draws, float* out, hipStream_t s);
 

@@ -781,6 +781,72 @@ hipError_t launch_uniforms(uint64_t seed, uint64_t stream, uint64_t rnd, int bat
   return hipGetLastError();
 }
 
+// ============================================================================
+// target tree layer set-up: row r of sequence b is tree row r, written to
+// cache row len_in[b] + r, seeing the prefix [0, len_in) and the tree rows of
+// its ancestor mask (bit j = cache row len_in + j); rows past n_nodes (or of
+// a sequence whose rows do not fit the cache) are padding
+// ============================================================================
+__global__ void target_rows_kernel(TargetRowsParams p) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.batch * p.n1) return;
+  const int b = idx / p.n1, r = idx - b * p.n1;
+  const int len = p.len_in[b];
+  const int n = p.n_nodes[b];
+  const bool ok = n >= 0 && n < p.n1 && len >= 0 &&
+                  static_cast<int64_t>(len) + p.n1 <= p.cap;
+  if (!ok && r == 0 && p.status != nullptr) atomicOr(p.status, 1 << 4);
+  const bool valid = ok && r <= n;
+  p.tok[idx] = valid ? p.token[idx] : -1;
+  p.pos[idx] = valid ? p.position[idx] : 0;
+  p.dest[idx] = ok ? len + r : 0;
+  p.plen[idx] = ok ? len : 0;
+  p.rmask[idx] = valid ? p.mask[static_cast<int64_t>(idx) * p.mask_words] : 0ull;
+  if (r == 0) p.sbase[b] = ok ? len : 0;
+}
+
+hipError_t launch_target_rows(const TargetRowsParams& p, hipStream_t s) {
+  const int n = p.batch * p.n1;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(target_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// x[row] = E[tok[row]] as fp32 (zero for padding rows) and the sums of
+// squares of its 16-column tiles, which the next GEMM's RMSNorm reads
+template <typename T>
+__global__ __launch_bounds__(64) void embed_rows_kernel(const T* embed, int vocab,
+                                                        const int32_t* tok, int H, float* x,
+                                                        float* ss) {
+  const int row = blockIdx.x;
+  const int t = tok[row];
+  const bool ok = t >= 0 && t < vocab;
+  const int ntile = H / 16;
+  for (int tile = threadIdx.x; tile < ntile; tile += 64) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = ok ? Elem<T>::to_f(embed[static_cast<int64_t>(t) * H + tile * 16 + i]) : 0.f;
+      x[static_cast<int64_t>(row) * H + tile * 16 + i] = v;
+      q += v * v;
+    }
+    ss[static_cast<int64_t>(row) * ntile + tile] = q;
+  }
+}
+
+template <typename T>
+hipError_t launch_embed_rows(const T* embed, int vocab, const int32_t* tok, int rows, int H,
+                             float* x, float* ss, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_rows_kernel<T>, dim3(rows), dim3(64), 0, s, embed, vocab, tok, H,
+                     x, ss);
+  return hipGetLastError();
+}
+template hipError_t launch_embed_rows<uint16_t>(const uint16_t*, int, const int32_t*, int, int,
+                                                float*, float*, hipStream_t);
+template hipError_t launch_embed_rows<float>(const float*, int, const int32_t*, int, int, float*,
+                                             float*, hipStream_t);
+
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;

@@ -294,6 +294,38 @@ eagle_status eagle_verify_tree_noalloc(
     int32_t *next_seed_rows, int32_t *next_seed_tokens, int32_t *next_seed_len,
     hipStream_t stream);
 
+/* (5) The target's verification forward over the flattened tree ([E1] "The
+ * Full Inference Loop", Phase 2: the target processes the prompt plus the
+ * draft tree in one forward pass under tree attention; [E3] 3.4 "The
+ * Inference Pipeline", Stage 2; [M75] 0x05C Target Verification), for a
+ * synthetic one-layer target: the context's weights are the target's (an
+ * eagle_create'd context of the target's shape; w_fuse and w_in are not
+ * used here).  For every sequence b and tree row r <= n_nodes[b]:
+ *   input      embed[token[b, r]]
+ *   RoPE       at position[b, r]
+ *   K/V        written to target cache row kv->len_in[b] + r
+ *   attends    the committed prefix [0, len_in[b]) and the cache rows
+ *              len_in[b] + j for the set bits j of mask[b, r, 0] (the row's
+ *              ancestors and itself, as eagle_draft_tree flattens them)
+ * then the decoder block and the LM head as in eagle_draft_step.
+ *   tree        the flattened trees (token, position, mask, n_nodes read)
+ *   kv          target cache, layout as eagle_kv; len_in [B] read, len_out
+ *               unused; needs len_in + budget + 1 <= cap (else ECAPACITY in
+ *               the status word and that sequence's rows are padding)
+ *   workspace   device, >= eagle_target_layer_workspace_bytes(cfg, batch)
+ *               bytes, 256-byte aligned, owned by the caller (scratch only)
+ *   hidden_out  [B, N+1, H] fp32 block outputs, or NULL
+ *   logits_out  [B, N+1, vocab] fp32 next-token logits after each row: the
+ *               target_logits eagle_verify_tree takes.
+ * Rows past n_nodes[b] are padding (zero logits).  Needs budget + 1 <= 64
+ * (one mask word), else EUNSUPPORTED.  Asynchronous on `stream`. */
+size_t eagle_target_layer_workspace_bytes(const eagle_config *cfg, int32_t batch);
+eagle_status eagle_target_tree_layer(eagle_ctx *ctx, int32_t batch,
+                                     const eagle_tree *tree, const eagle_kv *kv,
+                                     void *workspace, size_t ws_bytes,
+                                     float *hidden_out, float *logits_out,
+                                     hipStream_t stream);
+
 /* The draws the sampling steps use ([E1] Algorithm 1: "draw r ~ U(0,1)"):
  * out[b, r, j] = U(seed, stream_id; counter (j, r, b, round)) for b < batch,
  * r < rows, j < draws, as described at eagle_verify_tree.  out is fp32

@@ -53,7 +53,9 @@ __all__ = [
     "LOG_EPS", "bf16_round", "store", "Weights", "rmsnorm", "rope", "silu",
     "fuse", "layer", "topk_desc", "lse32", "child_logprob", "DraftKV",
     "draft_tree", "select_key", "eagle2_tree", "flatten", "verify", "verify_row",
-    "block", "tree_ancestors", "target_tree_layer",
+    "block", "tree_ancestors", "target_tree_layer", "gumbel_uniforms",
+    "sample_children", "draft_rows", "sampled_row_steps", "verify_row_sampled",
+    "verify_sampled",
     "commit", "decision_margin", "score_rows", "causal_attention", "attend",
     "philox4x64", "philox4x64_np", "uniform01", "verify_uniforms",
     "STREAM_VERIFY", "STREAM_DRAFT", "BONUS_DRAW",
@@ -341,7 +343,7 @@ def eagle2_tree(root, expand, width: int, max_depth: int, budget: int):
 
 
 def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
-               record: bool = False, d2t=None):
+               record: bool = False, d2t=None, sample=None):
     """Draft one tree for one sequence.
 
     Seed rows ([M75] 0x05A: [f_t, embed(x_{t+1})]) are appended to the draft
@@ -359,9 +361,22 @@ def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
     tokens, the embedding lookups and verification then use target ids; the
     map is increasing, so orders by draft id and by target id agree.
 
+    sample: dict(T, seed, rnd, b) for sampled children ([E1] 3.4: at T > 0
+    the children of a node are sampled from the draft distribution): each
+    expanded node's K children are sample_children draws from softmax(logits
+    / T) (Philox draws gumbel_uniforms of (seed, rnd, b, key row)), created in
+    draw order, with log confidence log q(x) = logits[x] / T - lse(logits /
+    T) in float32.  The budget must keep every created node (N >= K + (D-1)
+    K^2), so that the children a node shows are all of its draws, in order --
+    what the verification's sampling law needs.
+
     Mutates kv (seed rows + scratch rows).  Returns (tree, info)."""
     cfg = W.cfg
     K, D, N = cfg.K, cfg.D, cfg.N
+    if sample is not None:
+        if d2t is not None or N < cfg.n_cand:
+            raise ValueError("sampled children keep every drafted node: need "
+                             "N >= K + (D-1) K^2 and no reduced vocabulary")
     seed_src = np.atleast_2d(np.asarray(seed_src, dtype=np.float64))
     seed_tok = np.asarray(seed_tok, dtype=np.int64)
     s = len(seed_tok)
@@ -383,6 +398,17 @@ def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
         res = []
         for p in parents:
             lg = p["logits"]
+            if sample is not None:
+                T = sample["T"]
+                scaled = (np.asarray(lg, np.float32) / np.float32(T)).astype(np.float32)
+                lse = lse32(scaled)
+                key_row = 0 if p["id"] < 0 else 1 + p["id"]
+                u = gumbel_uniforms(sample["seed"], sample["rnd"], sample["b"], key_row,
+                                    len(lg))
+                ids, m = sample_children(lg, T, K, u)
+                info["sample_margin"] = min(info.get("sample_margin", float("inf")), m)
+                res.append([(t, child_logprob(scaled[t], lse)) for t in ids])
+                continue
             lse = lse32(lg)
             ids = sorted(int(i) for i in topk_desc(lg, K))
             res.append([(int(t) if d2t is None else int(d2t[t]),
@@ -414,7 +440,20 @@ def draft_tree(W: Weights, kv: DraftKV, seed_src, seed_tok, len_in: int,
     for n in selected:
         n["selected"] = True
     info["nodes"] = nodes
+    info["sampled"] = sample is not None
     return flatten(cfg, root, selected, p_root), info
+
+
+def draft_rows(cfg, tree, info) -> np.ndarray:
+    """Draft logits of the expanded nodes, float32 [1 + (D-1) K, V]: row 0
+    the root's, row 1 + s the node with scratch slot s (every node with
+    children in the tree was expanded and has a slot)."""
+    out = np.zeros((1 + max(cfg.D - 1, 0) * cfg.K, cfg.V), dtype=np.float32)
+    out[0] = info["root"]["logits"]
+    for n in info["nodes"]:
+        if n.get("slot", -1) >= 0 and "logits" in n:
+            out[1 + n["slot"]] = n["logits"]
+    return out
 
 
 def flatten(cfg, root, selected, p_root):
@@ -554,6 +593,9 @@ def decision_margin(cfg, tree_info) -> float:
     fin_low = allsc[min(N, len(allsc)) - 1] if N > 0 else inf
     if len(allsc) > N > 0:
         margin = min(margin, allsc[N - 1] - allsc[N])
+    if tree_info.get("sampled"):
+        # children are sampled: their draws decide, not per-row logit cuts
+        return min(margin, tree_info.get("sample_margin", inf))
     # per-row top-K cuts
     parents = {}
     for n in nodes:
@@ -657,6 +699,42 @@ def verify_uniforms(cfg, seed: int, rnd: int, b: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# sampled children ([E1] 3.4 "Tree-Structured Draft Generation": at T > 0 the
+# k children of a node are sampled from the draft distribution)
+# ---------------------------------------------------------------------------
+def gumbel_uniforms(seed: int, rnd: int, b: int, key_row, V: int) -> np.ndarray:
+    """U(0,1) draws for tokens 0..V-1 of one expanded node (float64): Philox
+    key (seed, STREAM_DRAFT), counter (x // 4, key_row, b, round), token x
+    takes output word x % 4; u = (top 24 bits + 1/2) * 2^-24, never 0 or 1.
+    key_row is 0 for the root and 1 + node id for a drafted node; an array
+    of key rows gives one row of draws per key [len, V]."""
+    rows = np.atleast_1d(np.asarray(key_row, dtype=np.uint64))
+    nq = (V + 3) // 4
+    q = np.broadcast_to(np.arange(nq, dtype=np.uint64)[None, :], (len(rows), nq))
+    kr = np.broadcast_to(rows[:, None], q.shape)
+    words = philox4x64_np(q, kr, np.full(q.shape, b, np.uint64),
+                          np.full(q.shape, rnd, np.uint64), seed, STREAM_DRAFT)
+    w = np.stack(words, axis=-1).reshape(len(rows), -1)[:, :V]
+    u = ((w >> np.uint64(40)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return u[0] if np.ndim(key_row) == 0 else u
+
+
+def sample_children(logits, T: float, K: int, u) -> tuple:
+    """K children drawn from q = softmax(logits / T) without replacement,
+    in draw order: the Gumbel-top-k construction (Gumbel-max applied K
+    times, each time over the tokens not yet drawn) -- x_i maximises
+    logits[x] / T + G(x), G(x) = -log(-log u[x]), over the remaining tokens,
+    ties to the lower id.  Returns (tokens, margin), margin = the smallest
+    gap between consecutive perturbed values among the first K + 1."""
+    lg = np.asarray(logits, dtype=np.float64)
+    key = lg / T - np.log(-np.log(np.asarray(u, dtype=np.float64)))
+    order = np.lexsort((np.arange(len(key)), -key))[: K + 1]
+    vals = key[order]
+    margin = float(np.min(vals[:-1] - vals[1:])) if len(vals) > 1 else float("inf")
+    return [int(x) for x in order[:K]], margin
+
+
+# ---------------------------------------------------------------------------
 # (4) verification
 # ---------------------------------------------------------------------------
 def verify_row(logits, child_tokens, T: float, u_child, u_bonus):
@@ -735,6 +813,104 @@ def verify(cfg, tree, target_logits, T: float, uniforms=None, seed=None,
         ci, tok, m = verify_row(target_logits[v], ktok, T,
                                 (lambda i: u[i]) if u is not None else None,
                                 (lambda: u[K]) if u is not None else None)
+        margin = min(margin, m)
+        if ci is not None:
+            v = kids[ci]
+            acc.append(v)
+            continue
+        bonus = tok
+        break
+    rows = np.full(D, -1, dtype=np.int32)
+    rows[: len(acc)] = acc
+    toks = np.full(D + 1, -1, dtype=np.int32)
+    for i, r in enumerate(acc):
+        toks[i] = tree["token"][r]
+    toks[len(acc)] = bonus
+    return {"accept_len": len(acc), "accepted_rows": rows, "tokens": toks,
+            "bonus": bonus, "margin": margin}
+
+
+def sampled_row_steps(target_logits, draft_logits, child_tokens, T: float):
+    """The quantities of Algorithm 1 of [E1] ("Verification Phase:
+    Multi-Round Speculative Sampling on Trees") at one row whose children
+    were drawn from q = softmax(draft / T) without replacement: p =
+    softmax(target / T); the i-th child's draft distribution p_hat_i is q
+    with the earlier children's tokens removed, renormalised; child i is
+    accepted with probability min(1, p(t_i) / p_hat_i(t_i)), and on
+    rejection p <- norm(max(0, p - p_hat_i)).  A residual of zero mass (p
+    equal to p_hat_i) restarts from the target distribution.
+    Returns (ratios [k], the residual p after all k rejections)."""
+    tl = np.asarray(target_logits, dtype=np.float64)
+    dl = np.asarray(draft_logits, dtype=np.float64)
+    p0 = np.exp((tl - tl.max()) / T)
+    p0 /= p0.sum()
+    q = np.exp((dl - dl.max()) / T)
+    q /= q.sum()
+    p = p0.copy()
+    drawn, ratios = [], []
+    for x in child_tokens:
+        prop = q.copy()
+        prop[drawn] = 0.0
+        prop /= prop.sum()
+        ratios.append(p[x] / prop[x])
+        res = np.maximum(0.0, p - prop)
+        z = res.sum()
+        p = res / z if z > 0.0 else p0.copy()
+        drawn.append(x)
+    return ratios, p
+
+
+def verify_row_sampled(target_logits, draft_logits, child_tokens, T: float,
+                       u_child, u_bonus):
+    """One visited row of the verification walk for sampled children
+    (sampled_row_steps): child i is accepted when u_i < ratio_i; if every
+    child is rejected, the emitted token is drawn from the final residual by
+    inverse CDF over ascending ids with u_bonus.
+    Returns (accepted child index or None, emitted token or None, margin)."""
+    ratios, p = sampled_row_steps(target_logits, draft_logits, child_tokens, T)
+    margin = float("inf")
+    for i, r in enumerate(ratios):
+        u = float(u_child(i))
+        margin = min(margin, abs(u - r))
+        if u < r:
+            return i, None, margin
+    ub = float(u_bonus())
+    cdf = np.cumsum(p)
+    cdf /= cdf[-1]
+    tok = int(np.searchsorted(cdf, ub, side="right"))
+    tok = min(tok, len(p) - 1)
+    while p[tok] == 0.0 and tok > 0:
+        tok -= 1
+    lo = cdf[tok - 1] if tok > 0 else 0.0
+    margin = min(margin, abs(ub - cdf[tok]), abs(ub - lo) if tok > 0 else 1.0)
+    return None, tok, margin
+
+
+def verify_sampled(cfg, tree, target_logits, draft_logit_rows, T: float,
+                   uniforms=None, seed=None, rnd: int = 0, b: int = 0):
+    """verify() for trees with sampled children: at each visited row v with
+    children, verify_row_sampled against that row's draft logits
+    (draft_logit_rows[0] for the root, [1 + kv_slot] for a drafted node);
+    children are taken in flattened order, which is their draw order.  A row
+    without children emits a token drawn from the target alone.  Draws as in
+    verify()."""
+    D, K = cfg.D, cfg.K
+    if uniforms is None and seed is not None:
+        uniforms = verify_uniforms(cfg, seed, rnd, b)
+    v = 0
+    acc = []
+    margin = float("inf")
+    while True:
+        fc, nc = int(tree["first_child"][v]), int(tree["n_child"][v])
+        kids = list(range(fc, fc + nc)) if nc > 0 else []
+        ktok = [int(tree["token"][c]) for c in kids]
+        u = uniforms[v]
+        if nc > 0:
+            e = 0 if v == 0 else 1 + int(tree["kv_slot"][v])
+            ci, tok, m = verify_row_sampled(target_logits[v], draft_logit_rows[e], ktok, T,
+                                            lambda i: u[i], lambda: u[K])
+        else:
+            ci, tok, m = verify_row(target_logits[v], [], T, None, lambda: u[K])
         margin = min(margin, m)
         if ci is not None:
             v = kids[ci]

@@ -228,6 +228,58 @@ class Drafter:
                                      _stream()), "eagle_draft_tree")
         return tree, len_out
 
+    def draft_tree_sampled(self, seed_src, seed_token, seed_len, kv: KVCache,
+                           temperature, seed, round=0, len_out=None, tree=None,
+                           draft_logits=None):
+        """draft_tree with K children sampled (without replacement) at every
+        expanded node.  Returns (tree, len_out, draft_logits [B, 1 + (D-1)K,
+        V] fp32)."""
+        B = seed_src.shape[0]
+        sh = self.shape
+        tree = tree if tree is not None else self.alloc_tree(B, seed_src.device)
+        len_out = len_out if len_out is not None else torch.empty(
+            B, dtype=torch.int32, device=seed_src.device)
+        ne = 1 + max(sh.depth - 1, 0) * sh.topk
+        if draft_logits is None:
+            draft_logits = torch.zeros(B, ne, sh.vocab, dtype=torch.float32,
+                                       device=seed_src.device)
+        ckv = kv.c_kv(kv.length, len_out)
+        ct = self._c_tree(tree)
+        check(lib().eagle_draft_tree_sampled(
+            self._ctx, B, _ptr(seed_src), _ptr(seed_token), _ptr(seed_len),
+            ctypes.byref(ckv), ctypes.byref(ct), float(temperature), int(seed),
+            int(round), _ptr(draft_logits), _stream()), "eagle_draft_tree_sampled")
+        return tree, len_out, draft_logits
+
+    def verify_sampled(self, tree, target_logits, draft_logits, temperature, seed=0,
+                       round=0, kv: KVCache | None = None, kv_len_out=None,
+                       commit_mode=_lib.COMMIT_KEEP):
+        """verify() for trees from draft_tree_sampled."""
+        B = tree["token"].shape[0]
+        D, S = self.shape.depth, self.shape.max_seed
+        i32 = dict(dtype=torch.int32, device=target_logits.device)
+        out = {"accept_len": torch.empty(B, **i32),
+               "accepted_rows": torch.empty(B, D, **i32),
+               "tokens": torch.empty(B, D + 1, **i32),
+               "seed_rows": torch.empty(B, S, **i32),
+               "seed_tokens": torch.empty(B, S, **i32),
+               "seed_len": torch.empty(B, **i32)}
+        ckv = None
+        if kv is not None:
+            if kv_len_out is None:
+                kv_len_out = torch.empty(B, **i32)
+            out["kv_len"] = kv_len_out
+            ckv = kv.c_kv(None, kv_len_out)
+        ct = self._c_tree(tree)
+        check(lib().eagle_verify_tree_sampled(
+            self._ctx, B, ctypes.byref(ct), _ptr(target_logits), _ptr(draft_logits),
+            float(temperature), int(seed), int(round), int(commit_mode),
+            ctypes.byref(ckv) if ckv is not None else None,
+            _ptr(out["accept_len"]), _ptr(out["accepted_rows"]), _ptr(out["tokens"]),
+            _ptr(out["seed_rows"]), _ptr(out["seed_tokens"]), _ptr(out["seed_len"]),
+            _stream()), "eagle_verify_tree_sampled")
+        return out
+
     def verify(self, tree, target_logits, temperature=0.0, seed=0, round=0,
                kv: KVCache | None = None, kv_len_out=None, out=None,
                commit_mode=_lib.COMMIT_KEEP, uniforms=None):

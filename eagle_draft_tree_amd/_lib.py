@@ -16,6 +16,7 @@ EXPORTS = ("eagle_workspace_bytes", "eagle_create", "eagle_destroy",
            "eagle_draft_step", "eagle_draft_tree", "eagle_verify_tree",
            "eagle_verify_tree_uniforms", "eagle_verify_tree_noalloc",
            "eagle_draw_uniforms", "eagle_target_layer_workspace_bytes",
+           "eagle_draft_tree_sampled", "eagle_verify_tree_sampled",
            "eagle_target_tree_layer",
            "eagle_profile", "eagle_profile_read")
 COMMIT_KEEP, COMMIT_RESEED = 0, 1
@@ -113,6 +114,15 @@ def lib():
     L.eagle_draw_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
                                       ctypes.c_uint64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, vp, vp]
+    L.eagle_draft_tree_sampled.restype = ctypes.c_int
+    L.eagle_draft_tree_sampled.argtypes = [vp, ctypes.c_int32, vp, vp, vp, ctypes.POINTER(KV),
+                                           ctypes.POINTER(Tree), ctypes.c_float,
+                                           ctypes.c_uint64, ctypes.c_uint64, vp, vp]
+    L.eagle_verify_tree_sampled.restype = ctypes.c_int
+    L.eagle_verify_tree_sampled.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Tree), vp, vp,
+                                            ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
+                                            ctypes.c_int32, ctypes.POINTER(KV), vp, vp, vp,
+                                            vp, vp, vp, vp]
     L.eagle_target_layer_workspace_bytes.restype = ctypes.c_size_t
     L.eagle_target_layer_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32]
     L.eagle_target_tree_layer.restype = ctypes.c_int

@@ -39,7 +39,7 @@ struct Offsets {
       lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
       c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
       len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
-      cnt_gemm, pack[7], apack;
+      cnt_gemm, pack[7], apack, orow;
   int R, Rpad, ncnt, ntile_lm, qg, ncand, max_split, apack_rows;
   int64_t part_elems;
   size_t total;
@@ -131,6 +131,7 @@ Offsets make_layout(const eagle_config& c) {
     const int kmax = std::max(std::max(3 * H, F), qd);
     f.apack = L.take(static_cast<size_t>(f.apack_rows) * ((kmax + 127) / 128 * 128) * 4);
   }
+  f.orow = L.take(R * 4);
   f.ntile_lm = (V + 63) / 64;
   f.lm_val = L.take(R * f.ntile_lm * c.topk * 4);
   f.lm_id = L.take(R * f.ntile_lm * c.topk * 4);
@@ -267,6 +268,14 @@ void prof_end(eagle_ctx* c, int i, hipStream_t s) {
     c->prof.overflow = true;
 }
 
+// Sampled children of a tree pass: where the expanded nodes' draft logits
+// go ([B, 1 + (D-1) K, V]) and the draw parameters.
+struct SampleSpec {
+  float* rows;
+  float T;
+  uint64_t seed, round;
+};
+
 struct Rows {  // one pass's query rows
   int batch, rps;
   const void* src;           // rows gathered through src_row (or identity)
@@ -278,6 +287,9 @@ struct Rows {  // one pass's query rows
   int32_t* topk_id;
   float* topk_val;
   float* lse;
+  const int32_t* node = nullptr;   // candidate id of each row (tree passes)
+  int pass = 0;                    // tree pass (1 = seed rows)
+  const SampleSpec* sample = nullptr;
 };
 
 template <typename T>
@@ -406,6 +418,24 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
       EAGLE_TRY(run_gemm<T>(c, scr, p, s));
       return EAGLE_OK;
     }
+    if (r.sample != nullptr) {
+      // sampled children: every logit of the expanded rows is kept (the
+      // verification needs their distributions), then K Gumbel-top-k draws
+      SampleParams sp;
+      sp.rows = R; sp.rows_per_seq = r.rps; sp.pass = r.pass; sp.K = cf.topk;
+      sp.V = cf.vocab; sp.NE = 1 + std::max(cf.depth - 1, 0) * cf.topk;
+      sp.T = r.sample->T; sp.seed = r.sample->seed; sp.round = r.sample->round;
+      sp.tok = r.tok; sp.dest = r.dest; sp.plen = r.plen; sp.node = r.node;
+      sp.out_row = c->at<int32_t>(c->off.orow); sp.logits = r.sample->rows;
+      sp.topk_id = r.topk_id; sp.topk_val = r.topk_val; sp.lse = r.lse;
+      EAGLE_TRY(launch_slot_rows(sp, s));
+      p.epi = EPI_STORE; p.out = r.sample->rows; p.ldo = cf.vocab; p.out_row = sp.out_row;
+      EAGLE_TRY(run_gemm<T>(c, scr, p, s));
+      const int pi = prof_begin(c, PC_MERGE, 0.0, 0.0, s);
+      EAGLE_TRY(launch_sample_children(sp, s));
+      prof_end(c, pi, s);
+      return EAGLE_OK;
+    }
     p.epi = EPI_LMHEAD;
     p.cand_val = scr.lm_val; p.cand_id = scr.lm_id;
     p.stat = scr.lm_stat; p.ntile_lm = scr.ntile_lm; p.topk = cf.topk;
@@ -476,7 +506,7 @@ template <typename T>
 eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
                              const int32_t* seed_token, const int32_t* seed_len,
                              const eagle_kv* kv, const eagle_tree* out,
-                             hipStream_t s) {
+                             hipStream_t s, const SampleSpec* sample = nullptr) {
   const eagle_config& cf = c->cfg;
   const Offsets& f = c->off;
   const int K = cf.topk, D = cf.depth, N = cf.budget;
@@ -508,6 +538,7 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
     r.a_out = c->at<char>(d % 2 ? f.a1 : f.a0);
     r.topk_id = c->at<int32_t>(f.tk_id); r.topk_val = c->at<float>(f.tk_val);
     r.lse = c->at<float>(f.lse);
+    r.node = cur.node; r.pass = d; r.sample = sample;
     eagle_status st = run_layer<T>(c, r, kv, s);
     if (st != EAGLE_OK) return st;
     GrowParams g;
@@ -517,6 +548,7 @@ eagle_status draft_tree_impl(eagle_ctx* c, int batch, const void* seed_src,
     g.topk_id = r.topk_id; g.topk_val = r.topk_val; g.lse = r.lse;
     g.cur = cur; g.nxt = nxt; g.ts = tree_state(c);
     g.seed_token = seed_token; g.seed_len = seed_len; g.d2t = c->w.d2t;
+    g.sampled = sample != nullptr;
     g.t_token = out->token; g.t_parent = out->parent; g.t_depth = out->depth;
     g.t_pos = out->position; g.t_slot = out->kv_slot; g.t_first = out->first_child;
     g.t_nchild = out->n_child; g.t_score = out->score; g.t_mask = out->mask;
@@ -805,6 +837,30 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_sr
                                       stream);
 }
 
+eagle_status eagle_draft_tree_sampled(eagle_ctx* ctx, int32_t batch, const void* seed_src,
+                                      const int32_t* seed_token, const int32_t* seed_len,
+                                      const eagle_kv* kv, const eagle_tree* out,
+                                      float temperature, uint64_t seed, uint64_t round,
+                                      float* draft_logits, hipStream_t stream) {
+  if (ctx == nullptr || kv == nullptr || null_tree(out) || draft_logits == nullptr)
+    return EAGLE_EINVAL;
+  const eagle_config& cf = ctx->cfg;
+  if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
+  if (!seed_src || !seed_token || !seed_len || !kv->k || !kv->v || !kv->len_in ||
+      !kv->len_out || kv->cap < 8 || kv->cap % 8)
+    return EAGLE_EINVAL;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return EAGLE_EINVAL;
+  // every draw stays in the tree, in draw order; one vocabulary
+  const int ncand = cf.depth > 0 ? cf.topk + (cf.depth - 1) * cf.topk * cf.topk : 0;
+  if (cf.budget < ncand || ctx->w.d2t != nullptr || cf.depth < 1) return EAGLE_EUNSUPPORTED;
+  const SampleSpec spec{draft_logits, temperature, seed, round};
+  return cf.dtype == EAGLE_BF16
+             ? draft_tree_impl<uint16_t>(ctx, batch, seed_src, seed_token, seed_len, kv,
+                                         out, stream, &spec)
+             : draft_tree_impl<float>(ctx, batch, seed_src, seed_token, seed_len, kv, out,
+                                      stream, &spec);
+}
+
 }  // extern "C"
 
 namespace {
@@ -824,7 +880,8 @@ eagle_status verify_core(const eagle_config& cf, const VerifyScratch& ws, eagle_
                          uint64_t round, int32_t commit_mode, const eagle_kv* kv_or_null,
                          int32_t* accept_len, int32_t* accepted_rows, int32_t* out_tokens,
                          int32_t* next_seed_rows, int32_t* next_seed_tokens,
-                         int32_t* next_seed_len, hipStream_t stream) {
+                         int32_t* next_seed_len, hipStream_t stream,
+                         const float* draft_rows = nullptr) {
   if (null_tree(tree)) return EAGLE_EINVAL;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
   if (!(temperature >= 0.f) || !std::isfinite(temperature)) return EAGLE_EINVAL;
@@ -858,6 +915,8 @@ eagle_status verify_core(const eagle_config& cf, const VerifyScratch& ws, eagle_
   p.kv_len = kv_or_null ? kv_or_null->len_out : nullptr;
   p.nkv = cf.n_kv_heads; p.hd = cf.head_dim; p.elem_bytes = esize(cf);
   p.status = ws.status;
+  p.draft_rows = draft_rows;
+  p.NE = 1 + std::max(cf.depth - 1, 0) * cf.topk;
   int pi = -1;
   if (prof != nullptr) {
     const double vbytes = static_cast<double>(batch) * (cf.budget + 1) * p.V * 4.0;
@@ -874,7 +933,8 @@ eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
                          int32_t commit_mode, const eagle_kv* kv_or_null,
                          int32_t* accept_len, int32_t* accepted_rows, int32_t* out_tokens,
                          int32_t* next_seed_rows, int32_t* next_seed_tokens,
-                         int32_t* next_seed_len, hipStream_t stream) {
+                         int32_t* next_seed_len, hipStream_t stream,
+                         const float* draft_rows = nullptr) {
   if (ctx == nullptr) return EAGLE_EINVAL;
   const Offsets& f = ctx->off;
   VerifyScratch ws;
@@ -885,7 +945,8 @@ eagle_status verify_impl(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
   ws.status = ctx->status();
   return verify_core(ctx->cfg, ws, ctx, batch, tree, target_logits, temperature, uniforms,
                      seed, round, commit_mode, kv_or_null, accept_len, accepted_rows,
-                     out_tokens, next_seed_rows, next_seed_tokens, next_seed_len, stream);
+                     out_tokens, next_seed_rows, next_seed_tokens, next_seed_len, stream,
+                     draft_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -943,6 +1004,22 @@ eagle_status eagle_verify_tree(eagle_ctx* ctx, int32_t batch, const eagle_tree* 
   return verify_impl(ctx, batch, tree, target_logits, temperature, nullptr, seed, round,
                      commit_mode, kv_or_null, accept_len, accepted_rows, out_tokens,
                      next_seed_rows, next_seed_tokens, next_seed_len, stream);
+}
+
+eagle_status eagle_verify_tree_sampled(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,
+                                       const float* target_logits, const float* draft_logits,
+                                       float temperature, uint64_t seed, uint64_t round,
+                                       int32_t commit_mode, const eagle_kv* kv_or_null,
+                                       int32_t* accept_len, int32_t* accepted_rows,
+                                       int32_t* out_tokens, int32_t* next_seed_rows,
+                                       int32_t* next_seed_tokens, int32_t* next_seed_len,
+                                       hipStream_t stream) {
+  if (ctx == nullptr || draft_logits == nullptr) return EAGLE_EINVAL;
+  if (!(temperature > 0.f)) return EAGLE_EINVAL;
+  if (ctx->w.d2t != nullptr) return EAGLE_EUNSUPPORTED;
+  return verify_impl(ctx, batch, tree, target_logits, temperature, nullptr, seed, round,
+                     commit_mode, kv_or_null, accept_len, accepted_rows, out_tokens,
+                     next_seed_rows, next_seed_tokens, next_seed_len, stream, draft_logits);
 }
 
 eagle_status eagle_verify_tree_uniforms(eagle_ctx* ctx, int32_t batch, const eagle_tree* tree,

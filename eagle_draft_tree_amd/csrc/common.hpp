@@ -198,9 +198,9 @@ constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
 constexpr uint64_t kStreamVerify = 0;   // key word 1 of verification draws
 constexpr uint64_t kStreamDraft = 1;    // key word 1 of drafting draws
 
-// first output word of the block at counter (c0, c1, c2, c3), key (k0, k1)
-__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t c2,
-                                                  uint64_t c3, uint64_t k0, uint64_t k1) {
+// the four output words of the block at counter (c0, c1, c2, c3), key (k0, k1)
+__device__ __forceinline__ void philox4x64(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                           uint64_t k0, uint64_t k1, uint64_t (&out)[4]) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
@@ -212,7 +212,18 @@ __device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint
     k0 += kPhiloxW0;
     k1 += kPhiloxW1;
   }
-  return c0;
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// first output word of the block at counter (c0, c1, c2, c3), key (k0, k1)
+__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                  uint64_t c3, uint64_t k0, uint64_t k1) {
+  uint64_t w[4];
+  philox4x64(c0, c1, c2, c3, k0, k1, w);
+  return w[0];
 }
 
 // U[0,1) float: counter (draw, row, sequence, round), key (seed, stream);

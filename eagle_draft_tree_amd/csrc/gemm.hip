@@ -313,7 +313,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
           const int m = m0 + mt * 16 + 4 * g + j;
           float y = acc[mt][ct][j];
           if (m < p.M && p.epi == EPI_RESID) y += p.resid[m * p.ldr + col];
-          if (m < p.M) out[m * p.ldo + col] = y;
+          if (m < p.M) {
+            const int64_t orow = p.out_row != nullptr ? p.out_row[m] : m;
+            if (orow >= 0) out[orow * p.ldo + col] = y;
+          }
           if (p.ss != nullptr) {
             float q = (m < p.M) ? y * y : 0.f;
             q += shfl_xor(q, 1);

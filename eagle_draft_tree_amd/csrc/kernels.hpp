@@ -56,6 +56,7 @@ struct GemmParams {
   int epi = EPI_STORE;
   void* out = nullptr;            // float activations (q: weight type)
   int64_t ldo = 0;
+  const int32_t* out_row = nullptr;  // STORE: output row of row m (< 0: dropped), or identity
   const float* resid = nullptr;
   int64_t ldr = 0;
   float* ss = nullptr;            // [M, N/16] sums of squares per 16-column tile
@@ -145,6 +146,7 @@ hipError_t launch_seed_setup(const SeedParams& p, hipStream_t s);
 
 struct GrowParams {
   int batch, K, D, N, pass, rows_per_seq, s_max;
+  int sampled = 0;      // children in draw order (sampled), else by token id
   const int32_t* d2t;   // draft id -> target id, or null (same vocabulary)
   const int32_t* topk_id; const float* topk_val; const float* lse;
   QueryDesc cur;      // this pass's rows
@@ -174,8 +176,35 @@ struct VerifyParams {
   void* kc; void* vc; int cap, nkv, hd; int32_t* kv_len;  // kc null: no commit
   int elem_bytes;
   int* status;
+  // sampled children: draft logits of the expanded nodes [B, NE, V] (row 0
+  // the root, 1 + kv_slot a drafted node), or null for point-mass children
+  const float* draft_rows = nullptr;
+  int NE = 0;
 };
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
+
+// sampled children of one pass: per query row with a draft-logit row
+// (out_row >= 0), K draws without replacement from softmax(logits / T) by
+// Gumbel-top-k with Philox (seed, draft stream) noise at counter
+// (token / 4, key row, sequence, round); writes the tokens in draw order,
+// logits / T of the drawn tokens and log-sum-exp(logits / T), in the layout
+// of the LM-head merge
+struct SampleParams {
+  int rows = 0, rows_per_seq = 0, pass = 0, K = 0, V = 0, NE = 0;
+  float T = 1.f;
+  uint64_t seed = 0, round = 0;
+  const int32_t* tok = nullptr;      // query rows (tok < 0: padding)
+  const int32_t* dest = nullptr;
+  const int32_t* plen = nullptr;
+  const int32_t* node = nullptr;     // candidate id of a pass >= 2 row
+  int32_t* out_row = nullptr;        // [rows] draft-logit row of each query row
+  const float* logits = nullptr;     // [B * NE, V]
+  int32_t* topk_id = nullptr;        // [rows, K]
+  float* topk_val = nullptr;
+  float* lse = nullptr;
+};
+hipError_t launch_slot_rows(const SampleParams& p, hipStream_t s);
+hipError_t launch_sample_children(const SampleParams& p, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 

@@ -295,8 +295,13 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
     const int row = p.pass == 1 ? b * p.s_max + p.seed_len[b] - 1 : b * K + rr;
     const int* ids = p.topk_id + static_cast<int64_t>(row) * K;
     const int my = ids[cc];
-    int rank = 0;
-    for (int j = 0; j < K; ++j) rank += ids[j] < my;
+    // children are created by ascending token id, or in draw order when
+    // they were sampled
+    int rank = cc;
+    if (!p.sampled) {
+      rank = 0;
+      for (int j = 0; j < K; ++j) rank += ids[j] < my;
+    }
     const int node = first + rr * K + rank;
     const int parent = p.pass == 1 ? -1 : p.cur.node[row];
     const float ps = parent < 0 ? 0.f : ts.c_score[cb + parent];
@@ -439,6 +444,137 @@ hipError_t launch_grow(const GrowParams& p, hipStream_t s) {
 }
 
 // ============================================================================
+// sampled children
+// ============================================================================
+// Draft-logit row of each query row of a pass: the root's row (the last seed
+// row of a sequence) in pass 1, 1 + scratch slot for a drafted node.
+__global__ void slot_rows_kernel(SampleParams p) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= p.rows) return;
+  const int b = m / p.rows_per_seq, i = m - b * p.rows_per_seq;
+  int orow = -1;
+  if (p.tok[m] >= 0) {
+    if (p.pass == 1) {
+      if (i + 1 == p.rows_per_seq || p.tok[m + 1] < 0) orow = b * p.NE;
+    } else {
+      const int slot = p.dest[m] - p.plen[m];
+      if (slot >= 0 && slot + 1 < p.NE) orow = b * p.NE + 1 + slot;
+    }
+  }
+  p.out_row[m] = orow;
+}
+
+hipError_t launch_slot_rows(const SampleParams& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_rows_kernel, dim3((p.rows + 255) / 256), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// Gumbel-top-k: the K largest logits[x] / T - log(-log u_x), best first,
+// ties to the lower id, are K draws without replacement from
+// softmax(logits / T) in draw order.  Each thread keeps a sorted top-K of
+// its tokens; K rounds of a wave argmax and one sort over the four waves'
+// lists give the row's.
+__global__ __launch_bounds__(256) void sample_children_kernel(SampleParams p) {
+  __shared__ float sv[4 * kMaxTopK];
+  __shared__ int si[4 * kMaxTopK];
+  __shared__ float red_m[4], red_s[4];
+  const int m = blockIdx.x;
+  const int orow = p.out_row[m];
+  if (orow < 0) return;
+  const int K = p.K;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int b = m / p.rows_per_seq;
+  const uint64_t key_row = p.pass == 1 ? 0ull : 1ull + static_cast<uint64_t>(p.node[m]);
+  const float* lg = p.logits + static_cast<int64_t>(orow) * p.V;
+  const float invT = 1.f / p.T;
+  float lv[kMaxTopK];
+  int li[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+  float mx = -INFINITY;
+  for (int q4 = threadIdx.x; q4 * 4 < p.V; q4 += 256) {
+    uint64_t w[4];
+    philox4x64(static_cast<uint64_t>(q4), key_row, static_cast<uint64_t>(b), p.round, p.seed,
+               kStreamDraft, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int x = q4 * 4 + k;
+      if (x >= p.V) break;
+      const float l = lg[x];
+      mx = fmaxf(mx, l);
+      const float u = (static_cast<float>(w[k] >> 40) + 0.5f) * 5.9604644775390625e-08f;
+      const float key = l / p.T - logf(-logf(u));
+#pragma unroll
+      for (int j = kMaxTopK - 1; j >= 0; --j) {
+        if (j >= K) continue;
+        if (better(key, x, lv[j], li[j])) {
+          if (j > 0 && better(key, x, lv[j - 1], li[j - 1])) {
+            lv[j] = lv[j - 1];
+            li[j] = li[j - 1];
+          } else {
+            lv[j] = key;
+            li[j] = x;
+          }
+        }
+      }
+    }
+  }
+  // log-sum-exp of logits / T
+  const float m_all = [&] {
+    const float wm = wave_max(mx);
+    if (lane == 0) red_m[wave] = wm;
+    __syncthreads();
+    return fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  }();
+  float se = 0.f;
+  for (int x = threadIdx.x; x < p.V; x += 256) se += expf((lg[x] - m_all) * invT);
+  se = wave_sum(se);
+  if (lane == 0) red_s[wave] = se;
+  // the wave's K best, then all four waves' lists sorted by one wave
+  for (int r = 0; r < K; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = shfl_xor(bv, o);
+      const int oi = shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lv[0] == bv && li[0] == bi) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK - 1; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+      lv[kMaxTopK - 1] = -INFINITY;
+      li[kMaxTopK - 1] = 0x7fffffff;
+    }
+    if (lane == 0) { sv[wave * K + r] = bv; si[wave * K + r] = bi; }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v = lane < 4 * K ? sv[lane] : -INFINITY;
+    int id = lane < 4 * K ? si[lane] : 0x7fffffff;
+    wave_sort_desc(v, id);
+    if (lane < K) {
+      const int x = id;
+      p.topk_id[static_cast<int64_t>(m) * K + lane] = x;
+      p.topk_val[static_cast<int64_t>(m) * K + lane] =
+          (x >= 0 && x < p.V) ? lg[x] / p.T : -INFINITY;
+    }
+    if (lane == 0) {
+      const float S = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+      p.lse[m] = m_all / p.T + logf(S);
+    }
+  }
+}
+
+hipError_t launch_sample_children(const SampleParams& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  if (p.K < 1 || p.K > kMaxTopK || p.T <= 0.f) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_children_kernel, dim3(p.rows), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
 // verification
 // ============================================================================
 __device__ __forceinline__ float wexp(float l, float m, float T) {
@@ -507,12 +643,213 @@ __device__ __forceinline__ float draw_uniform(const VerifyParams& p, int b, int 
                         static_cast<uint64_t>(v), static_cast<uint64_t>(j));
 }
 
+// Block-wide sum of one double per thread (s: 256 doubles of LDS); every
+// thread gets the total.
+__device__ __forceinline__ double block_sum_d(double v, double* s) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  s[tid] = v;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) s[tid] += s[tid + w];
+    __syncthreads();
+  }
+  const double t = s[0];
+  __syncthreads();
+  return t;
+}
+
+// The walk of a tree with sampled children, by the whole workgroup
+// (Algorithm 1 of the verification with per-child draft distributions: the
+// children of a row were drawn from q = softmax(draft / T) without
+// replacement, so the i-th child's distribution is q without the earlier
+// children, renormalised).  With p = softmax(target / T), the residual after
+// i rejections is (p(y) - C(y) q(y))+ / N_i, C(y) = C_i for tokens not yet
+// drawn and frozen at C_j for the j-th drawn token, where C_0 = 0, N_0 = 1,
+// C_i = C_(i-1) + N_(i-1) / R_i and R_i is the q mass not drawn before
+// child i; child i is accepted when u_i < (p - C_(i-1) q)+(x_i) R_i /
+// (N_(i-1) q(x_i)).  A residual of zero mass restarts from p.  Rows without
+// children, and rows whose children were all rejected, emit a token drawn
+// from the residual by inverse CDF over ascending ids.
+__device__ void sampled_walk(const VerifyParams& p, int b, int* s_acc, int* s_a_out,
+                             int* s_bonus_out, int* s_bad_out, double* s_red, int* s_pick) {
+  __shared__ int s_v, s_fc, s_nc, s_stop, s_acc_n, s_bad, s_nd, s_take;
+  __shared__ double s_C, s_N, s_R;
+  __shared__ int s_dx[kMaxTopK];
+  __shared__ double s_dc[kMaxTopK];
+  __shared__ float s_mq;
+  const int tid = threadIdx.x;
+  const int rows1 = p.N + 1;
+  const int64_t ob = static_cast<int64_t>(b) * rows1;
+  const float T = p.T;
+  if (tid == 0) { s_v = 0; s_acc_n = 0; s_bad = 0; s_stop = 0; }
+  __syncthreads();
+  while (true) {
+    if (tid == 0) {
+      const int v = s_v;
+      const int fc = p.t_first[ob + v], nc = p.t_nchild[ob + v];
+      if (p.row_bad[ob + v] || nc < 0 || nc > kMaxTopK ||
+          (nc > 0 && (fc < 1 || fc + nc > rows1)))
+        s_bad = 1;
+      if (nc > 0) {
+        const int e = v == 0 ? 0 : 1 + p.t_slot[ob + v];
+        if (e < 0 || e >= p.NE) s_bad = 1;
+        for (int j = 0; j < nc && !s_bad; ++j) {
+          const int t = p.t_token[ob + fc + j];
+          if (t < 0 || t >= p.V) s_bad = 1;
+        }
+      }
+      s_fc = fc;
+      s_nc = nc;
+      s_C = 0.0; s_N = 1.0; s_R = 1.0; s_nd = 0;
+    }
+    __syncthreads();
+    if (s_bad) break;
+    const int v = s_v, fc = s_fc, nc = s_nc;
+    const float* tl = p.logits + (ob + v) * p.V;
+    const float mt = p.row_max[ob + v];
+    const double St = p.row_sum[ob + v];
+    const float* dl = nullptr;
+    double Sq = 1.0;
+    if (nc > 0) {
+      const int e = v == 0 ? 0 : 1 + p.t_slot[ob + v];
+      dl = p.draft_rows + (static_cast<int64_t>(b) * p.NE + e) * p.V;
+      float mq = -INFINITY;
+      for (int i = tid; i < p.V; i += 256) mq = fmaxf(mq, dl[i]);
+      mq = wave_max(mq);
+      if ((tid & 63) == 0) s_pick[tid >> 6] = __float_as_int(mq);
+      __syncthreads();
+      if (tid == 0) {
+        float m = -INFINITY;
+        for (int w = 0; w < 4; ++w) m = fmaxf(m, __int_as_float(s_pick[w]));
+        s_mq = m;
+      }
+      __syncthreads();
+      double part = 0.0;
+      for (int i = tid; i < p.V; i += 256) part += static_cast<double>(wexp(dl[i], s_mq, T));
+      Sq = block_sum_d(part, s_red);
+    }
+    const float mq = s_mq;
+    auto pt = [&](int y) { return static_cast<double>(wexp(tl[y], mt, T)) / St; };
+    auto qd = [&](int y) { return static_cast<double>(wexp(dl[y], mq, T)) / Sq; };
+    int accepted = -1;
+    for (int i = 0; i < nc; ++i) {
+      if (tid == 0) {
+        const int x = p.t_token[ob + fc + i];
+        const double px = pt(x), qx = qd(x);
+        const double num = fmax(0.0, px - s_C * qx) * s_R;
+        const double den = s_N * qx;
+        const double u = static_cast<double>(draw_uniform(p, b, v, i));
+        s_take = (den <= 0.0) ? (num > 0.0) : (u * den < num);
+        if (!s_take) {
+          const double Cn = s_C + s_N / s_R;
+          s_dx[s_nd] = x;
+          s_dc[s_nd] = Cn;
+          s_nd += 1;
+          s_R -= qx;
+          s_C = Cn;
+        }
+      }
+      __syncthreads();
+      if (s_take) { accepted = i; break; }
+      // N_i: the bulk at the new C, then the tokens drawn before this one
+      // at their frozen C
+      const double C = s_C;
+      double part = 0.0;
+      for (int y = tid; y < p.V; y += 256) part += fmax(0.0, pt(y) - C * qd(y));
+      const double bulk = block_sum_d(part, s_red);
+      if (tid == 0) {
+        double Nn = bulk;
+        for (int j = 0; j + 1 < s_nd; ++j) {
+          const int y = s_dx[j];
+          Nn += fmax(0.0, pt(y) - s_dc[j] * qd(y)) - fmax(0.0, pt(y) - C * qd(y));
+        }
+        if (Nn > 0.0) {
+          s_N = Nn;
+        } else {  // zero-mass residual: start again from p
+          s_C = 0.0;
+          s_N = 1.0;
+          s_nd = 0;
+        }
+      }
+      __syncthreads();
+    }
+    if (accepted >= 0) {
+      if (tid == 0) {
+        if (s_acc_n >= p.D || s_acc_n >= kMaxPath) {
+          s_bad = 1;
+        } else {
+          s_acc[s_acc_n++] = fc + accepted;
+          s_v = fc + accepted;
+        }
+      }
+      __syncthreads();
+      if (s_bad) break;
+      continue;
+    }
+    // ---- emitted token: inverse CDF of the residual over ascending ids ----
+    const double C = s_C;
+    const int nd = s_nd;
+    auto wres = [&](int y) {
+      if (dl == nullptr) return pt(y);
+      double c = C;
+      for (int j = 0; j < nd; ++j)
+        if (s_dx[j] == y) c = s_dc[j];
+      return fmax(0.0, pt(y) - c * qd(y));
+    };
+    const int per = (p.V + 255) / 256;
+    const int lo = tid * per, hi = min(p.V, lo + per);
+    double mine = 0.0;
+    for (int y = lo; y < hi; ++y) mine += wres(y);
+    __syncthreads();
+    s_red[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const double t = tid >= off ? s_red[tid - off] : 0.0;
+      __syncthreads();
+      s_red[tid] += t;
+      __syncthreads();
+    }
+    const double total = s_red[255];
+    const double excl = s_red[tid] - mine;
+    const double thr = static_cast<double>(draw_uniform(p, b, v, kBonusDraw)) * total;
+    int pick = -1, lastnz = -1;
+    double cum = excl;
+    for (int y = lo; y < hi; ++y) {
+      const double w = wres(y);
+      if (w > 0.0) lastnz = y;
+      if (pick < 0 && w > 0.0 && thr >= excl) {
+        cum += w;
+        if (cum > thr) pick = y;
+      }
+    }
+    __syncthreads();
+    s_pick[tid] = pick;
+    s_pick[256 + tid] = lastnz;
+    __syncthreads();
+    if (tid == 0) {
+      int best = -1, last = -1;
+      for (int t = 0; t < 256 && best < 0; ++t) best = s_pick[t];
+      for (int t = 0; t < 256; ++t) last = max(last, s_pick[256 + t]);
+      *s_bonus_out = best >= 0 ? best : last;
+      if (*s_bonus_out < 0) s_bad = 1;
+    }
+    __syncthreads();
+    break;
+  }
+  if (tid == 0) {
+    *s_a_out = s_acc_n;
+    *s_bad_out = s_bad;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
   __shared__ int s_kids[kMaxTopK];
   __shared__ int s_nk, s_row, s_need_res, s_bad, s_a, s_bonus;
   __shared__ int s_acc[kMaxPath];
   __shared__ double s_part[256];
-  __shared__ int s_pick[256];
+  __shared__ int s_pick[512];
   __shared__ int s_kept[kMaxPath];
   __shared__ int s_nkept;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -530,138 +867,143 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
     return;
   }
 
-  if (tid == 0) {
-    int v = 0, a = 0, bad = 0, need = 0, bonus = -1;
-    while (true) {
-      if (p.row_bad[ob + v]) { bad = 1; break; }
-      const int fc = p.t_first[ob + v], nc = p.t_nchild[ob + v];
-      if (nc < 0 || nc > kMaxTopK || (nc > 0 && (fc < 1 || fc + nc > rows1))) {
-        bad = 1;
-        break;
-      }
-      const float* lg = p.logits + (ob + v) * p.V;
-      int nxt = -1;
-      if (p.T == 0.f) {
-        const int x = p.row_arg[ob + v];
-        for (int j = 0; j < nc; ++j)
-          if (p.t_token[ob + fc + j] == x) nxt = fc + j;
-        if (nxt < 0) { bonus = x; break; }
-      } else {
-        double S = p.row_sum[ob + v];
-        const float mx = p.row_max[ob + v];
-        for (int j = 0; j < nc; ++j) {
-          const int tok = p.t_token[ob + fc + j];
-          if (tok < 0 || tok >= p.V) { bad = 1; break; }
-          s_kids[j] = tok;
-          const double w = static_cast<double>(wexp(lg[tok], mx, p.T));
-          const float u = draw_uniform(p, b, v, j);
-          if (static_cast<double>(u) * S < w) { nxt = fc + j; break; }
-          S -= w;
-        }
-        if (bad) break;
-        if (nxt < 0) {
-          need = 1;
-          s_nk = nc;
+  if (p.draft_rows != nullptr) {
+    sampled_walk(p, b, s_acc, &s_a, &s_bonus, &s_bad, s_part, s_pick);
+    __syncthreads();
+  } else {
+    if (tid == 0) {
+      int v = 0, a = 0, bad = 0, need = 0, bonus = -1;
+      while (true) {
+        if (p.row_bad[ob + v]) { bad = 1; break; }
+        const int fc = p.t_first[ob + v], nc = p.t_nchild[ob + v];
+        if (nc < 0 || nc > kMaxTopK || (nc > 0 && (fc < 1 || fc + nc > rows1))) {
+          bad = 1;
           break;
         }
+        const float* lg = p.logits + (ob + v) * p.V;
+        int nxt = -1;
+        if (p.T == 0.f) {
+          const int x = p.row_arg[ob + v];
+          for (int j = 0; j < nc; ++j)
+            if (p.t_token[ob + fc + j] == x) nxt = fc + j;
+          if (nxt < 0) { bonus = x; break; }
+        } else {
+          double S = p.row_sum[ob + v];
+          const float mx = p.row_max[ob + v];
+          for (int j = 0; j < nc; ++j) {
+            const int tok = p.t_token[ob + fc + j];
+            if (tok < 0 || tok >= p.V) { bad = 1; break; }
+            s_kids[j] = tok;
+            const double w = static_cast<double>(wexp(lg[tok], mx, p.T));
+            const float u = draw_uniform(p, b, v, j);
+            if (static_cast<double>(u) * S < w) { nxt = fc + j; break; }
+            S -= w;
+          }
+          if (bad) break;
+          if (nxt < 0) {
+            need = 1;
+            s_nk = nc;
+            break;
+          }
+        }
+        if (a >= p.D || a >= kMaxPath) { bad = 1; break; }  // malformed tree
+        s_acc[a++] = nxt;
+        v = nxt;
       }
-      if (a >= p.D || a >= kMaxPath) { bad = 1; break; }  // malformed tree
-      s_acc[a++] = nxt;
-      v = nxt;
+      s_row = v;
+      s_need_res = need;
+      s_bad = bad;
+      s_a = a;
+      s_bonus = bonus;
     }
-    s_row = v;
-    s_need_res = need;
-    s_bad = bad;
-    s_a = a;
-    s_bonus = bonus;
-  }
-  __syncthreads();
-
-  if (s_need_res && !s_bad) {
-    // residual draw at row v: children's tokens removed, inverse CDF
-    const int v = s_row;
-    const float* lg = p.logits + (ob + v) * p.V;
-    const float mx = p.row_max[ob + v];
-    const int nk = s_nk;
-    const int per = (p.V + 255) / 256;
-    const int lo = tid * per, hi = min(p.V, lo + per);
-    double part = 0.0;
-    for (int i = lo; i < hi; ++i) {
-      bool kid = false;
-      for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
-      if (!kid) part += static_cast<double>(wexp(lg[i], mx, p.T));
-    }
-    s_part[tid] = part;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const double t = tid >= off ? s_part[tid - off] : 0.0;
-      __syncthreads();
-      s_part[tid] += t;
-      __syncthreads();
-    }
-    const double total = s_part[255];
-    const double excl = s_part[tid] - part;
-    const double u = static_cast<double>(draw_uniform(p, b, v, kBonusDraw));
-    const double thr = u * total;
-    int pick = -1;
-    if (total > 0.0) {
-      if (thr >= excl && thr < excl + part) {
-        double cum = excl;
-        for (int i = lo; i < hi && pick < 0; ++i) {
-          bool kid = false;
-          for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
-          if (kid) continue;
-          cum += static_cast<double>(wexp(lg[i], mx, p.T));
-          if (cum > thr) pick = i;
-        }
-      }
-      s_pick[tid] = pick;
-      __syncthreads();
-      if (tid == 0) {
-        int best = -1;
-        for (int t = 0; t < 256 && best < 0; ++t) best = s_pick[t];
-        s_bonus = best;
-      }
-      __syncthreads();
-      if (s_bonus < 0) {  // rounding put the threshold past the last mass
-        int lastnz = -1;
-        for (int i = lo; i < hi; ++i) {
-          bool kid = false;
-          for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
-          if (!kid && wexp(lg[i], mx, p.T) > 0.f) lastnz = i;
-        }
-        s_pick[tid] = lastnz;
-        __syncthreads();
-        if (tid == 0) {
-          int best = -1;
-          for (int t = 0; t < 256; ++t) best = max(best, s_pick[t]);
-          s_bonus = best;
-        }
-      }
-    } else {
-      // the children held all the mass: best remaining token
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+
+    if (s_need_res && !s_bad) {
+      // residual draw at row v: children's tokens removed, inverse CDF
+      const int v = s_row;
+      const float* lg = p.logits + (ob + v) * p.V;
+      const float mx = p.row_max[ob + v];
+      const int nk = s_nk;
+      const int per = (p.V + 255) / 256;
+      const int lo = tid * per, hi = min(p.V, lo + per);
+      double part = 0.0;
       for (int i = lo; i < hi; ++i) {
         bool kid = false;
         for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
-        if (!kid && better(lg[i], i, bv, bi)) { bv = lg[i]; bi = i; }
+        if (!kid) part += static_cast<double>(wexp(lg[i], mx, p.T));
       }
-      s_part[tid] = bv;
-      s_pick[tid] = bi;
+      s_part[tid] = part;
       __syncthreads();
-      if (tid == 0) {
-        float best = -INFINITY;
-        int bid = 0x7fffffff;
-        for (int t = 0; t < 256; ++t)
-          if (better(static_cast<float>(s_part[t]), s_pick[t], best, bid)) {
-            best = static_cast<float>(s_part[t]);
-            bid = s_pick[t];
-          }
-        s_bonus = bid;
+      for (int off = 1; off < 256; off <<= 1) {
+        const double t = tid >= off ? s_part[tid - off] : 0.0;
+        __syncthreads();
+        s_part[tid] += t;
+        __syncthreads();
       }
+      const double total = s_part[255];
+      const double excl = s_part[tid] - part;
+      const double u = static_cast<double>(draw_uniform(p, b, v, kBonusDraw));
+      const double thr = u * total;
+      int pick = -1;
+      if (total > 0.0) {
+        if (thr >= excl && thr < excl + part) {
+          double cum = excl;
+          for (int i = lo; i < hi && pick < 0; ++i) {
+            bool kid = false;
+            for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+            if (kid) continue;
+            cum += static_cast<double>(wexp(lg[i], mx, p.T));
+            if (cum > thr) pick = i;
+          }
+        }
+        s_pick[tid] = pick;
+        __syncthreads();
+        if (tid == 0) {
+          int best = -1;
+          for (int t = 0; t < 256 && best < 0; ++t) best = s_pick[t];
+          s_bonus = best;
+        }
+        __syncthreads();
+        if (s_bonus < 0) {  // rounding put the threshold past the last mass
+          int lastnz = -1;
+          for (int i = lo; i < hi; ++i) {
+            bool kid = false;
+            for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+            if (!kid && wexp(lg[i], mx, p.T) > 0.f) lastnz = i;
+          }
+          s_pick[tid] = lastnz;
+          __syncthreads();
+          if (tid == 0) {
+            int best = -1;
+            for (int t = 0; t < 256; ++t) best = max(best, s_pick[t]);
+            s_bonus = best;
+          }
+        }
+      } else {
+        // the children held all the mass: best remaining token
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int i = lo; i < hi; ++i) {
+          bool kid = false;
+          for (int j = 0; j < nk; ++j) kid |= s_kids[j] == i;
+          if (!kid && better(lg[i], i, bv, bi)) { bv = lg[i]; bi = i; }
+        }
+        s_part[tid] = bv;
+        s_pick[tid] = bi;
+        __syncthreads();
+        if (tid == 0) {
+          float best = -INFINITY;
+          int bid = 0x7fffffff;
+          for (int t = 0; t < 256; ++t)
+            if (better(static_cast<float>(s_part[t]), s_pick[t], best, bid)) {
+              best = static_cast<float>(s_part[t]);
+              bid = s_pick[t];
+            }
+          s_bonus = bid;
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- outputs, next seed, commit ----

@@ -232,6 +232,34 @@ eagle_status eagle_draft_tree(eagle_ctx *ctx, int32_t batch,
                               const int32_t *seed_len, const eagle_kv *kv,
                               const eagle_tree *out, hipStream_t stream);
 
+/* (2)+(3) eagle_draft_tree with sampled children ([E1] 3.4 "Tree-Structured
+ * Draft Generation": at temperature > 0 the k children of a node are sampled
+ * from the draft distribution).  Each expanded node (the root, then the K
+ * nodes each pass expands) draws its K children from q = softmax(logits /
+ * temperature) without replacement, by Gumbel-top-k: the K largest
+ * logits[x] / temperature - log(-log u_x), ties to the lower id, in that
+ * order; u_x = (top 24 bits of Philox4x64-10 word x % 4 + 1/2) * 2^-24 with
+ * key (seed, EAGLE_STREAM_DRAFT) and counter (x / 4, key row, b, round), the
+ * key row 0 for the root and 1 + the node's creation index (the order in
+ * which the passes create candidates, K per expanded node) otherwise.  A
+ * child's value is its parent's plus log q(x).  Every draw stays in the tree:
+ * needs budget >= K + (D-1) K^2 (so the final top-N keeps all) and no d2t,
+ * else EUNSUPPORTED; depth >= 1; temperature > 0 (EINVAL).  Siblings are
+ * flattened in draw order (rows still ordered by depth, then parent row).
+ *   draft_logits [B, 1 + (D-1) K, vocab] fp32, written: row 0 the root's
+ *                logits, row 1 + s those of the node with scratch slot s --
+ *                the q of every row that has children, for
+ *                eagle_verify_tree_sampled.
+ * Other arguments as eagle_draft_tree. */
+eagle_status eagle_draft_tree_sampled(eagle_ctx *ctx, int32_t batch,
+                                      const void *seed_src,
+                                      const int32_t *seed_token,
+                                      const int32_t *seed_len,
+                                      const eagle_kv *kv, const eagle_tree *out,
+                                      float temperature, uint64_t seed,
+                                      uint64_t round, float *draft_logits,
+                                      hipStream_t stream);
+
 /* (4) Verify each sequence's tree ([E1] "Verification Phase: Multi-Round
  * Speculative Sampling on Trees", Algorithm 1; "The Full Inference Loop":
  * a >= 0 accepted draft tokens plus one emitted token) and commit.
@@ -265,6 +293,25 @@ eagle_status eagle_verify_tree(eagle_ctx *ctx, int32_t batch,
                                int32_t *out_tokens, int32_t *next_seed_rows,
                                int32_t *next_seed_tokens,
                                int32_t *next_seed_len, hipStream_t stream);
+
+/* eagle_verify_tree for trees drafted by eagle_draft_tree_sampled:
+ * Algorithm 1 of [E1] ("Verification Phase: Multi-Round Speculative Sampling
+ * on Trees") with p = softmax(target_logits / T) and, for the i-th child (in
+ * draw order) of a row, p_hat_i = softmax(draft_logits[row] / T) with the
+ * earlier children's tokens removed and renormalised: child i is accepted
+ * when u_i < p(t_i) / p_hat_i(t_i), else p <- norm(max(0, p - p_hat_i)); if
+ * all are rejected (or the row has no children) the emitted token is drawn
+ * from p by inverse CDF over ascending ids.  A residual of zero mass
+ * restarts from the target distribution.  Draws, commit and outputs as
+ * eagle_verify_tree.  draft_logits as eagle_draft_tree_sampled wrote them.
+ * temperature > 0, else EINVAL; a context with d2t is EUNSUPPORTED. */
+eagle_status eagle_verify_tree_sampled(
+    eagle_ctx *ctx, int32_t batch, const eagle_tree *tree,
+    const float *target_logits, const float *draft_logits, float temperature,
+    uint64_t seed, uint64_t round, int32_t commit_mode,
+    const eagle_kv *kv_or_null, int32_t *accept_len, int32_t *accepted_rows,
+    int32_t *out_tokens, int32_t *next_seed_rows, int32_t *next_seed_tokens,
+    int32_t *next_seed_len, hipStream_t stream);
 
 /* eagle_verify_tree with explicit draws instead of Philox (the same
  * Algorithm 1 of [E1]): uniforms [B, N+1, K+1] fp32 in [0,1), column i < K

@@ -101,8 +101,12 @@ def test_sampled_verify_matches_oracle(T):
             base = O.score_rows(m.oracle, s.kv, s.tree, s.info).astype(np.float64)
             for att in range(30):
                 noise = synth.normal(synth.GenKey(3, "sv", s.b, rnd, att), base.shape, std=2.0)
-                # sharpened towards the drafter so children get accepted
+                # sharpened towards the drafter so children get accepted; in
+                # round 0 the target of sequence 0 is the drafter itself, so
+                # every visited row with children accepts its first child
                 t = ((base + noise) * (3.0 if rnd % 2 else 1.0)).astype(np.float32)
+                if rnd == 0 and s.b == 0:
+                    t = base.astype(np.float32)
                 w = O.verify_sampled(cfg, s.tree, t, rows[s.b], T, seed=SEED, rnd=rnd, b=s.b)
                 if w["margin"] >= 1e-6:
                     break
@@ -114,6 +118,9 @@ def test_sampled_verify_matches_oracle(T):
         for b, s in enumerate(seqs):
             want = O.verify_sampled(cfg, s.tree, tl[b], rows[b], T, seed=SEED, rnd=rnd, b=b)
             accepted += want["accept_len"]
+            if rnd == 0 and b == 0:
+                # each visited row accepts its first child until a leaf
+                assert want["accept_len"] >= 1, "target = drafter accepts the first child"
             assert int(res["accept_len"][b]) == want["accept_len"], (rnd, b)
             assert np.array_equal(res["tokens"][b].cpu().numpy(), want["tokens"]), (rnd, b)
             okv = s.kv.copy()

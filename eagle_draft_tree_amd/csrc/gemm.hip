@@ -109,27 +109,41 @@ __device__ __forceinline__ void a_values(const GemmParams& p, const float* rn, i
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
   if (row >= p.M || k >= kend) return;
-  int si = 0, base = 0;
-  if (p.nseg > 1 && k >= p.seg[0].width) {
-    base = p.seg[0].width;
-    si = 1;
-    if (p.nseg > 2 && k >= base + p.seg[1].width) {
-      base += p.seg[1].width;
-      si = 2;
-    }
-  }
-  const ASeg& sg = si == 0 ? p.seg[0] : (si == 1 ? p.seg[1] : p.seg[2]);
+  // the segment holding k; its fields are picked lane by lane from the
+  // three (uniform) descriptors -- indexing the descriptor array by a
+  // per-lane segment would read the kernel arguments through vector loads,
+  // each one waiting for every load in flight, weights included
+  const ASeg &s0 = p.seg[0], &s1 = p.seg[1], &s2 = p.seg[2];
+  const int w0 = s0.width, w01 = s0.width + s1.width;
+  const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+  const int kk = k - (si == 0 ? 0 : (si == 1 ? w0 : w01));
+  const void* base = si == 0 ? s0.base : (si == 1 ? s1.base : s2.base);
+  const int64_t ld = si == 0 ? s0.ld : (si == 1 ? s1.ld : s2.ld);
+  const int32_t* rowidx = si == 0 ? s0.rowidx : (si == 1 ? s1.rowidx : s2.rowidx);
+  const int rowlimit = si == 0 ? s0.rowlimit : (si == 1 ? s1.rowlimit : s2.rowlimit);
+  const int f32 = si == 0 ? s0.f32 : (si == 1 ? s1.f32 : s2.f32);
   int r = row;
-  if (sg.rowidx != nullptr) {
-    r = sg.rowidx[row];
-    if (r < 0 || r >= sg.rowlimit) return;
+  if (rowidx != nullptr) {
+    r = rowidx[row];
+    if (r < 0 || r >= rowlimit) return;
   }
-  const int kk = k - base;
-  load8<T>(sg, r, kk, v);
-  if (sg.f32 && sg.ss != nullptr) {
+  if (f32) {
+    const float* src = static_cast<const float*>(base) + r * ld + kk;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
+  } else {
+    Frag8<T> w;
+    w.load(static_cast<const T*>(base) + r * ld + kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = w.get(i);
+  }
+  // RMSNorm (segment 0 only): row factor and gain
+  if (si == 0 && s0.f32 && s0.ss != nullptr) {
     const float f = rn[m];
     Frag8<T> gv;
-    gv.load(static_cast<const T*>(sg.gain) + kk);
+    gv.load(static_cast<const T*>(s0.gain) + kk);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
   }
@@ -349,10 +363,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
 // device-scope release fence would do the same by writing back the whole
 // L2 of the XCD, which costs more than the GEMM.  Returns true in the
 // workgroup that arrived last, with acc holding the sum over splits in
-// split order; ctr is that tile's arrival counter (left at zero).
+// split order; ctr is that tile's arrival counter (left at zero).  lds
+// holds at least the 16 MT x 64 CT tile in fp32.
 template <int MT, int CT>
 __device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT][CT],
-                                            int group, int m0, int split, int* ctr) {
+                                            unsigned char* lds, int group, int m0, int split,
+                                            int* ctr) {
   __shared__ int last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -382,24 +398,46 @@ __device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT
   }
   __syncthreads();
   if (!last) return false;
+  // The last workgroup sums the partials of its 16 MT x 64 CT tile in
+  // split order: each thread takes tile elements four at a time and issues
+  // all of their split loads before adding any (one memory round trip per
+  // group of four, not one per split), the sums are staged in LDS and each
+  // lane then takes its accumulators back in fragment layout.
+  constexpr int kMaxS = 16, kCh = 4;
+  constexpr int rows = 16 * MT, cols = 64 * CT;
+  float* red = reinterpret_cast<float*>(lds);
+  for (int e0 = threadIdx.x; e0 < rows * cols; e0 += 256 * kCh) {
+    float part[kCh][kMaxS];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int tile = (group * 4 + wave) * CT + ct;
+    for (int i = 0; i < kCh; ++i) {
+      const int e = e0 + i * 256;
+      const int m = m0 + e / cols, col = group * cols + e % cols;
+      const bool ok = e < rows * cols && m < p.M && col < p.N;
+      const float* src = p.part + static_cast<int64_t>(m) * p.N + col;
+#pragma unroll
+      for (int sp = 0; sp < kMaxS; ++sp)
+        part[i][sp] = (ok && sp < p.S)
+                          ? __hip_atomic_load(src + static_cast<int64_t>(sp) * p.Mtot * p.N,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const int e = e0 + i * 256;
+      float sum = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kMaxS; ++sp) sum += part[i][sp];
+      if (e < rows * cols) red[e] = sum;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = m0 + mt * 16 + 4 * g + j;
-        float sum = 0.f;
-        if (m < p.M && tile < ntiles) {
-          for (int sp = 0; sp < p.S; ++sp)
-            sum += __hip_atomic_load(
-                p.part + (static_cast<int64_t>(sp) * p.Mtot + m) * p.N + tile * 16 + c,
-                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        acc[mt][ct][j] = sum;
-      }
-  }
+      for (int j = 0; j < 4; ++j)
+        acc[mt][ct][j] = red[(mt * 16 + 4 * g + j) * cols + (wave * CT + ct) * 16 + c];
   return true;
 }
 
@@ -500,7 +538,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
 
   if (p.S > 1) {
     const int ngroups = (ntiles + 4 * CT - 1) / (4 * CT);
-    if (!splitk_last<MT, CT>(p, acc, group, m0, split, p.cnt + blockIdx.z * ngroups + group))
+    if (!splitk_last<MT, CT>(p, acc, lds, group, m0, split,
+                             p.cnt + blockIdx.z * ngroups + group))
       return;
   }
   epilogue<T, MT, CT>(p, acc, lds, group, m0);
@@ -639,7 +678,8 @@ __global__ __launch_bounds__(256) void dense_gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  if (p.S > 1 && !splitk_last<MT, CT>(p, acc, group, m0, split, p.cnt + rb * ngroups + group))
+  if (p.S > 1 &&
+      !splitk_last<MT, CT>(p, acc, lds, group, m0, split, p.cnt + rb * ngroups + group))
     return;
   epilogue<T, MT, CT>(p, acc, lds, group, m0);
 }
@@ -696,7 +736,7 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
     const int RB = (p.M + 63) / 64, ngroups = (ntiles + 15) / 16;
     const int ksteps = (p.K + kStep - 1) / kStep;
     int S = 1;
-    while (RB * ngroups * S < (3 * num_cus) / 2 && ksteps / (S + 1) >= 4 &&
+    while (RB * ngroups * S < (3 * num_cus) / 2 && ksteps / (S + 1) >= 4 && S < 16 &&
            static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
       ++S;
     const int steps = (ksteps + S - 1) / S;
@@ -720,7 +760,7 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   // least two steps
   int S = 1;
   if (ngroups * chunks < num_cus)
-    while (ngroups * chunks * S < 2 * num_cus && (ksteps + S) / (S + 1) >= 2) ++S;
+    while (ngroups * chunks * S < 2 * num_cus && (ksteps + S) / (S + 1) >= 2 && S < 16) ++S;
   // the partial sums must fit the workspace
   while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
   const int steps = (ksteps + S - 1) / S;

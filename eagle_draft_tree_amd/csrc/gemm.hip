@@ -441,6 +441,138 @@ __device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT
   return true;
 }
 
+// ---- pipelined A staging (bf16, up to 32 rows) --------------------------
+// A piece (PS steps of 128 k for 16 MT rows) is fetched into registers one
+// piece ahead: its loads are issued before the weight loads of the piece
+// being multiplied, so waiting for them (in-order completion) leaves that
+// piece's weight stream in flight.  Each thread always handles the same
+// rows.  The segment descriptors and the gathered source row of every
+// (row, segment) sit in LDS, where lanes index them freely (indexing the
+// kernel arguments or a register array by a per-lane segment would put
+// them in memory).
+template <int NG>
+struct APipe {
+  uint32_t raw[NG][8];   // fp32 values, or bf16 pairs in raw[0..3]
+  u32x4 gain[NG];        // RMSNorm gain (bf16) of the 8 columns
+};
+
+struct ASegLds {
+  const void* base[3];
+  int64_t ld[3];
+  int f32[3];
+  int row[32][3];        // source row per (row of the chunk, segment), -1 = zero
+};
+
+template <int MT>
+__device__ __forceinline__ void a_tables(const GemmParams& p, ASegLds& t, int m0) {
+  const int tid = threadIdx.x;
+  if (tid < 3) {
+    const ASeg& sg = p.seg[tid < p.nseg ? tid : 0];
+    t.base[tid] = sg.base;
+    t.ld[tid] = sg.ld;
+    t.f32[tid] = sg.f32;
+  }
+  if (tid < 16 * MT * 3) {
+    const int m = tid / 3, si = tid % 3;
+    const int row = m0 + m;
+    int r = -1;
+    if (row < p.M && si < p.nseg) {
+      const ASeg& sg = si == 0 ? p.seg[0] : (si == 1 ? p.seg[1] : p.seg[2]);
+      r = row;
+      if (sg.rowidx != nullptr) {
+        r = sg.rowidx[row];
+        if (r < 0 || r >= sg.rowlimit) r = -1;
+      }
+    }
+    t.row[m][si] = r;
+  }
+}
+
+template <typename T, int MT, int PS, int NG>
+__device__ __forceinline__ void a_fetch(const GemmParams& p, const ASegLds& t, APipe<NG>& ap,
+                                        int k0, int kend) {
+  constexpr int K8N = PS * 16;
+  const int w0 = p.seg[0].width, w01 = p.seg[0].width + p.seg[1].width;
+  const bool norm0 = p.seg[0].f32 && p.seg[0].ss != nullptr;
+  const T* gain0 = static_cast<const T*>(p.seg[0].gain);
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int idx = static_cast<int>(threadIdx.x) + 256 * j;
+    const int m = idx / K8N;
+    const int k = k0 + 8 * (idx % K8N);
+    const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+    const int kk = k - (si == 0 ? 0 : (si == 1 ? w0 : w01));
+    const bool inrow = m < 16 * MT;
+    const int r = inrow ? t.row[m][si] : -1;
+    const bool ok = k < kend && r >= 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ap.raw[j][i] = 0u;
+    if (ok) {
+      const int64_t off = static_cast<int64_t>(r) * t.ld[si] + kk;
+      if (t.f32[si]) {
+        const float* src = static_cast<const float*>(t.base[si]) + off;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { ap.raw[j][i] = x0[i]; ap.raw[j][4 + i] = x1[i]; }
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const T*>(t.base[si]) + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ap.raw[j][i] = x[i];
+      }
+    }
+    ap.gain[j] = (ok && si == 0 && norm0) ? *reinterpret_cast<const u32x4*>(gain0 + kk)
+                                          : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T, int MT, int PS, int NG>
+__device__ __forceinline__ void a_store(const GemmParams& p, const ASegLds& t,
+                                        const APipe<NG>& ap, unsigned char* lds,
+                                        const float* rn, int k0, int np) {
+  constexpr int K8N = PS * 16;
+  const int w0 = p.seg[0].width, w01 = p.seg[0].width + p.seg[1].width;
+  const bool norm0 = p.seg[0].f32 && p.seg[0].ss != nullptr;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int idx = static_cast<int>(threadIdx.x) + 256 * j;
+    const int m = idx / K8N, k8 = idx % K8N;
+    const int st = k8 >> 4, rem = k8 & 15;
+    if (m >= 16 * MT || st >= np) continue;
+    const int k = k0 + 8 * k8;
+    const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+    float v[8];
+    if (t.f32[si]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ap.raw[j][i]);
+    } else {
+      Frag8<uint16_t> w;
+      w.v = u32x4{ap.raw[j][0], ap.raw[j][1], ap.raw[j][2], ap.raw[j][3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = w.get(i);
+    }
+    if (si == 0 && norm0) {
+      const float f = rn[m];
+      Frag8<uint16_t> gv;
+      gv.v = ap.gain[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
+    }
+    const int g = rem >> 2, e = rem & 3;
+    const int mt = m >> 4, c = m & 15;
+    const int lane = g * 16 + c;
+    unsigned char* blk = lds + static_cast<size_t>((st * 4 + e) * MT + mt) * kBlk;
+    u32x4 hi, lo;
+    split_hi_lo(v, hi, lo);
+    *reinterpret_cast<u32x4*>(blk + lane * 16) = hi;
+    *reinterpret_cast<u32x4*>(blk + 1024 + lane * 16) = lo;
+  }
+  // the zero block read by padding steps
+  unsigned char* zb = lds + static_cast<size_t>(np * 4 * MT) * kBlk;
+  for (int i = threadIdx.x; i < kBlk / 16; i += 256)
+    *reinterpret_cast<u32x4*>(zb + i * 16) = u32x4{0u, 0u, 0u, 0u};
+}
+
 template <typename T, int MT, int CT, int PS>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
   // weight steps in flight per wave; a piece of PS steps is fully unrolled,
@@ -478,14 +610,26 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
       for (int e = 0; e < 4; ++e) wf[ct][e].load_nt(wtile[ct] + sc * step_stride + e * kPackBlk);
   };
 
+  // order of the first loads: the row factors and the gathered rows, then
+  // the first piece of A, then the first PF steps of weights -- waiting for
+  // the A loads when staging them (in-order completion) leaves the weights
+  // in flight
   __shared__ float rn[16 * MT];
   row_factors<MT>(p, rn, m0);
+  constexpr bool kPipe = sizeof(T) == 2 && MT <= 2;
+  constexpr int NG = kPipe ? (MT * 16 * PS * 16 + 255) / 256 : 1;
+  APipe<NG> ap;
+  __shared__ ASegLds at;
+  if constexpr (kPipe) {
+    a_tables<MT>(p, at, m0);
+    __syncthreads();
+    a_fetch<T, MT, PS, NG>(p, at, ap, st0 * kStep, kend);
+  }
   __syncthreads();
 
   Frag8<T> wb[PF][CT][4];
 #pragma unroll
   for (int i = 0; i < PF; ++i) load_w(st0 + i, wb[i]);
-  // the first PF steps of weights are in flight while A is staged
   __builtin_amdgcn_sched_barrier(0);
 
   f32x4 acc[MT][CT];
@@ -497,8 +641,16 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
   for (int ps0 = 0; ps0 < nsteps; ps0 += PS) {
     const int np = min(PS, nsteps - ps0);
     if (ps0 > 0) __syncthreads();  // every wave is done with the last piece
-    fill_a<T, MT>(p, lds, rn, m0, (st0 + ps0) * kStep, kend, np);
-    __syncthreads();
+    if constexpr (kPipe) {
+      a_store<T, MT, PS, NG>(p, at, ap, lds, rn, (st0 + ps0) * kStep, np);
+      __syncthreads();
+      // the next piece's A, ahead of this piece's weight refills
+      if (ps0 + PS < nsteps) a_fetch<T, MT, PS, NG>(p, at, ap, (st0 + ps0 + PS) * kStep, kend);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      fill_a<T, MT>(p, lds, rn, m0, (st0 + ps0) * kStep, kend, np);
+      __syncthreads();
+    }
     const int zero_blk = np * 4 * MT;
 #pragma unroll
     for (int s = 0; s < PS; ++s) {

@@ -21,12 +21,18 @@ constexpr float kLogEps = -27.631021115928547f;  // log(1e-12) in float32
 __device__ __forceinline__ float bf2f(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
-// round to nearest even; NaN kept quiet
+// Round to nearest even through the hardware conversion (v_cvt_pk_bf16_f32,
+// NaN stays NaN).  A bit-level rounding in software costs a divergent branch
+// per value for the NaN case, which made staging fp32 activations as bf16
+// pairs a large part of the streaming GEMM's time.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// two values in one 32-bit word: a in the low half, b in the high half
+__device__ __forceinline__ uint32_t f2bf_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // Element traits.  T is the storage type: uint16_t (bf16 bits) or float.
@@ -62,10 +68,7 @@ template <> struct Frag8<uint16_t> {
     uint32_t w = v[i >> 1];
     return bf2f(static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xffffu)));
   }
-  __device__ __forceinline__ void set_pair(int j, float lo, float hi) {
-    v[j] = static_cast<uint32_t>(f2bf(lo)) |
-           (static_cast<uint32_t>(f2bf(hi)) << 16);
-  }
+  __device__ __forceinline__ void set_pair(int j, float lo, float hi) { v[j] = f2bf_pair(lo, hi); }
   __device__ __forceinline__ void set(int i, float x) {
     uint32_t w = v[i >> 1];
     uint32_t b = f2bf(x);

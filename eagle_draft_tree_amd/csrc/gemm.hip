@@ -83,11 +83,15 @@ __device__ __forceinline__ void load8(const ASeg& sg, int64_t row, int kk, float
 
 // RMSNorm factors of rows m0 .. m0 + 16 MT of segment 0 (the only one that
 // may be normalised) from the producer's per-16-column sums of squares:
-// 1 / sqrt(mean(y^2) + eps), one value per row into rn.
+// 1 / sqrt(mean(y^2) + eps), one value per row into rn (1 when segment 0 is
+// not normalised).
 template <int MT>
 __device__ __forceinline__ void row_factors(const GemmParams& p, float* rn, int m0) {
   const ASeg& sg = p.seg[0];
-  if (!sg.f32 || sg.ss == nullptr) return;
+  if (!sg.f32 || sg.ss == nullptr) {
+    for (int r = threadIdx.x; r < 16 * MT; r += 256) rn[r] = 1.f;
+    return;
+  }
   constexpr int TPR = 256 / (16 * MT);  // threads per row: 16, 8, 4
   const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
   const int row = m0 + r;
@@ -450,11 +454,28 @@ __device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT
 // (row, segment) sit in LDS, where lanes index them freely (indexing the
 // kernel arguments or a register array by a per-lane segment would put
 // them in memory).
+// 16 bytes through a pointer that was read from LDS, as a global load: the
+// compiler cannot tell such a pointer's address space and would emit a flat
+// load, which also counts against the LDS counter, so that every later wait
+// for an LDS read would wait for it and for the weight loads issued before it
+__device__ __forceinline__ u32x4 load_global16(const void* ptr) {
+  typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
+  return *(const global_u32x4*)ptr;
+}
+
+// A thread stages the same 8 columns of A (k8 = thread % (16 PS)) in rows
+// thread / (16 PS) + j * 256 / (16 PS), j < NG: one gain load serves all rows.
 template <int NG>
 struct APipe {
   uint32_t raw[NG][8];   // fp32 values, or bf16 pairs in raw[0..3]
-  u32x4 gain[NG];        // RMSNorm gain (bf16) of the 8 columns
+  u32x4 gain;            // RMSNorm gain (bf16) of the 8 columns, or ones
 };
+
+// What lanes with nothing to stage load instead: 32 zero bytes (values) and
+// eight bf16 ones (the gain of columns that are not normalised), so that
+// staging needs no masks.
+__device__ __attribute__((aligned(64))) uint32_t g_stage_fill[12] = {
+    0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
 struct ASegLds {
   const void* base[3];
@@ -488,77 +509,91 @@ __device__ __forceinline__ void a_tables(const GemmParams& p, ASegLds& t, int m0
   }
 }
 
+// Every lane issues the same loads whatever its rows, segment or bounds
+// (two per row group and the gain; lanes with nothing to load read
+// g_stage_fill): with loads under branches the compiler can only count the
+// smallest number issued, and the wait for the next weight step would then
+// also wait for the A loads issued after it -- draining the weight stream at
+// every piece.
 template <typename T, int MT, int PS, int NG>
 __device__ __forceinline__ void a_fetch(const GemmParams& p, const ASegLds& t, APipe<NG>& ap,
                                         int k0, int kend) {
   constexpr int K8N = PS * 16;
+  static_assert(256 % K8N == 0, "a thread keeps its columns across row groups");
+  const int tid = threadIdx.x;
   const int w0 = p.seg[0].width, w01 = p.seg[0].width + p.seg[1].width;
   const bool norm0 = p.seg[0].f32 && p.seg[0].ss != nullptr;
   const T* gain0 = static_cast<const T*>(p.seg[0].gain);
+  const char* zeros = reinterpret_cast<const char*>(g_stage_fill);
+  const int k = k0 + 8 * (tid % K8N);
+  const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+  const int kk = k - (si == 0 ? 0 : (si == 1 ? w0 : w01));
+  const bool kin = k < kend;
+  const int f32 = t.f32[si];
+  const char* base = static_cast<const char*>(t.base[si]);
+  const int64_t ld = t.ld[si];
+  const int esz = f32 ? 4 : static_cast<int>(sizeof(T));
+  const bool gok = kin && si == 0 && norm0;
+  ap.gain = load_global16(gok ? static_cast<const void*>(gain0 + kk)
+                              : static_cast<const void*>(g_stage_fill + 8));
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const int idx = static_cast<int>(threadIdx.x) + 256 * j;
-    const int m = idx / K8N;
-    const int k = k0 + 8 * (idx % K8N);
-    const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
-    const int kk = k - (si == 0 ? 0 : (si == 1 ? w0 : w01));
-    const bool inrow = m < 16 * MT;
-    const int r = inrow ? t.row[m][si] : -1;
-    const bool ok = k < kend && r >= 0;
+    const int m = tid / K8N + j * (256 / K8N);
+    const int r = t.row[m][si];
+    const bool ok = kin && r >= 0;
+    const char* src = ok ? base + (static_cast<int64_t>(r) * ld + kk) * esz : zeros;
+    // bf16 rows hold their 8 values in 16 bytes: the second load repeats it
+    const u32x4 x0 = load_global16(src);
+    const u32x4 x1 = load_global16(ok && f32 ? src + 16 : src);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ap.raw[j][i] = 0u;
-    if (ok) {
-      const int64_t off = static_cast<int64_t>(r) * t.ld[si] + kk;
-      if (t.f32[si]) {
-        const float* src = static_cast<const float*>(t.base[si]) + off;
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { ap.raw[j][i] = x0[i]; ap.raw[j][4 + i] = x1[i]; }
-      } else {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const T*>(t.base[si]) + off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ap.raw[j][i] = x[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      ap.raw[j][i] = x0[i];
+      ap.raw[j][4 + i] = x1[i];
     }
-    ap.gain[j] = (ok && si == 0 && norm0) ? *reinterpret_cast<const u32x4*>(gain0 + kk)
-                                          : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
+// Stage the fetched piece in LDS: mask, RMSNorm factor and gain, bf16 hi + lo
+// split, fragment order.  Selects only, no per-value branches.  Groups past
+// the slice hold zeros (their loads were masked), so the padding steps of a
+// last, partial piece read zero blocks.  Rows past M are skipped: their
+// blocks were zeroed once, before the first piece, with the block after the
+// piece (index PS * 4 * MT).  A wave stages one row (PS >= 4), so the skip is
+// uniform across it.
 template <typename T, int MT, int PS, int NG>
 __device__ __forceinline__ void a_store(const GemmParams& p, const ASegLds& t,
                                         const APipe<NG>& ap, unsigned char* lds,
-                                        const float* rn, int k0, int np) {
+                                        const float* rn, int m0, int k0) {
   constexpr int K8N = PS * 16;
+  static_assert(NG * 256 == 16 * MT * K8N, "the groups cover the piece exactly");
+  const int tid = threadIdx.x;
   const int w0 = p.seg[0].width, w01 = p.seg[0].width + p.seg[1].width;
-  const bool norm0 = p.seg[0].f32 && p.seg[0].ss != nullptr;
+  const int k8 = tid % K8N;
+  const int st = k8 >> 4, rem = k8 & 15;
+  const int g = rem >> 2, e = rem & 3;
+  const int k = k0 + 8 * k8;
+  const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+  const bool f32 = t.f32[si] != 0;
+  float gn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t gw = ap.gain[i >> 1];
+    gn[i] = __uint_as_float((i & 1) ? (gw & 0xffff0000u) : (gw << 16));
+  }
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const int idx = static_cast<int>(threadIdx.x) + 256 * j;
-    const int m = idx / K8N, k8 = idx % K8N;
-    const int st = k8 >> 4, rem = k8 & 15;
-    if (m >= 16 * MT || st >= np) continue;
-    const int k = k0 + 8 * k8;
-    const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+    const int m = tid / K8N + j * (256 / K8N);
+    if (m0 + m >= p.M) continue;
+    // the row factor applies to segment 0 only (it is 1 when that segment
+    // is not normalised); masked values are zeros, masked gains ones
+    const float f = si == 0 ? rn[m] : 1.f;
     float v[8];
-    if (t.f32[si]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(ap.raw[j][i]);
-    } else {
-      Frag8<uint16_t> w;
-      w.v = u32x4{ap.raw[j][0], ap.raw[j][1], ap.raw[j][2], ap.raw[j][3]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = w.get(i);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = ap.raw[j][i >> 1];
+      const float vb = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+      v[i] = (f32 ? __uint_as_float(ap.raw[j][i]) : vb) * f * gn[i];
     }
-    if (si == 0 && norm0) {
-      const float f = rn[m];
-      Frag8<uint16_t> gv;
-      gv.v = ap.gain[j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
-    }
-    const int g = rem >> 2, e = rem & 3;
     const int mt = m >> 4, c = m & 15;
     const int lane = g * 16 + c;
     unsigned char* blk = lds + static_cast<size_t>((st * 4 + e) * MT + mt) * kBlk;
@@ -567,10 +602,6 @@ __device__ __forceinline__ void a_store(const GemmParams& p, const ASegLds& t,
     *reinterpret_cast<u32x4*>(blk + lane * 16) = hi;
     *reinterpret_cast<u32x4*>(blk + 1024 + lane * 16) = lo;
   }
-  // the zero block read by padding steps
-  unsigned char* zb = lds + static_cast<size_t>(np * 4 * MT) * kBlk;
-  for (int i = threadIdx.x; i < kBlk / 16; i += 256)
-    *reinterpret_cast<u32x4*>(zb + i * 16) = u32x4{0u, 0u, 0u, 0u};
 }
 
 template <typename T, int MT, int CT, int PS>
@@ -622,6 +653,10 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
   __shared__ ASegLds at;
   if constexpr (kPipe) {
     a_tables<MT>(p, at, m0);
+    // every block zero once: rows past M are never staged, and the block
+    // after the piece is the one padding steps read
+    for (int i = threadIdx.x; i < (PS * 4 * MT + 1) * kBlk / 16; i += 256)
+      *reinterpret_cast<u32x4*>(lds + i * 16) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     a_fetch<T, MT, PS, NG>(p, at, ap, st0 * kStep, kend);
   }
@@ -642,16 +677,19 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
     const int np = min(PS, nsteps - ps0);
     if (ps0 > 0) __syncthreads();  // every wave is done with the last piece
     if constexpr (kPipe) {
-      a_store<T, MT, PS, NG>(p, at, ap, lds, rn, (st0 + ps0) * kStep, np);
+      a_store<T, MT, PS, NG>(p, at, ap, lds, rn, m0, (st0 + ps0) * kStep);
       __syncthreads();
-      // the next piece's A, ahead of this piece's weight refills
-      if (ps0 + PS < nsteps) a_fetch<T, MT, PS, NG>(p, at, ap, (st0 + ps0 + PS) * kStep, kend);
+      // the next piece's A, ahead of this piece's weight refills; issued
+      // after the last piece too (every lane then reads the dummy address),
+      // so that the number of loads in flight is the same on every path and
+      // the waits for the weights below count past these loads
+      a_fetch<T, MT, PS, NG>(p, at, ap, (st0 + ps0 + PS) * kStep, kend);
       __builtin_amdgcn_sched_barrier(0);
     } else {
       fill_a<T, MT>(p, lds, rn, m0, (st0 + ps0) * kStep, kend, np);
       __syncthreads();
     }
-    const int zero_blk = np * 4 * MT;
+    const int zero_blk = (kPipe ? PS : np) * 4 * MT;
 #pragma unroll
     for (int s = 0; s < PS; ++s) {
       const int i = s % PF;

@@ -144,21 +144,37 @@ __device__ __forceinline__ f32x4 mfma16(const Frag8<float>& a,
 // ----------------------------------------------------------------------------
 // wave helpers
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ float shfl_xor(float v, int m) {
-  return __shfl_xor(v, m, kWave);
-}
+// Lane i gets the value of lane i ^ m.  Masks 1 and 2 are DPP quad
+// permutations and 8 a DPP rotation by 8 within each 16-lane row (both plain
+// VALU moves); 4 and 16 are ds_swizzle in bit mode (within 32 lanes, no LDS
+// access); 32 and anything else go through ds_bpermute.  The callers' loops
+// are unrolled, so m is a constant and the choice folds away.
 __device__ __forceinline__ int shfl_xor(int v, int m) {
-  return __shfl_xor(v, m, kWave);
+  switch (m) {
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 4: return __builtin_amdgcn_ds_swizzle(v, (4 << 10) | 0x1F);
+    case 16: return __builtin_amdgcn_ds_swizzle(v, (16 << 10) | 0x1F);
+    default: return __shfl_xor(v, m, kWave);
+  }
 }
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  return __int_as_float(shfl_xor(__float_as_int(v), m));
+}
+// Wave-wide max / sum, the same value in every lane: a butterfly within each
+// 32-lane half, then the two halves' results combined (half 0 first).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-  return v;
+  for (int m = 1; m <= 16; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
-  return v;
+  for (int m = 1; m <= 16; m <<= 1) v += shfl_xor(v, m);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
 }
 
 // (value, id) order used by every top-k: larger value first, then lower id

@@ -77,30 +77,39 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   __shared__ float sv[kSurv];
   __shared__ int si[kSurv];
   __shared__ float red_a[4], red_b[4];
-  __shared__ int nsurv;
+  __shared__ int nsurv, ntl;
+  __shared__ int stile[kSurv];
   const int row = blockIdx.x;
   if (p.tok[row] < 0) return;
   const int K = p.topk;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int64_t base = static_cast<int64_t>(row) * p.ntile;
-  if (threadIdx.x == 0) nsurv = 0;
+  if (threadIdx.x == 0) { nsurv = 0; ntl = 0; }
 
-  // ---- tile statistics: log-sum-exp, and this thread's tile maxima ----
+  // ---- tile statistics: log-sum-exp, and this thread's tile maxima.  All
+  // of a thread's (max, sum) pairs are loaded before any is used (indices
+  // clamped into the row), so they cost one memory round trip ----
   constexpr int kTPT = 8;   // tile maxima per thread in registers
   const bool fast = p.ntile <= 256 * kTPT;
   float hmax[kTPT];
   float M = -INFINITY, S = 0.f;
+  {
+    float2 st[kTPT];
 #pragma unroll
-  for (int u = 0; u < kTPT; ++u) {
-    const int t = threadIdx.x + 256 * u;
-    hmax[u] = -INFINITY;
-    if (t >= p.ntile) continue;
-    const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
-    hmax[u] = mx;
-    if (mx == -INFINITY) continue;
-    const float nm = fmaxf(M, mx);
-    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
-    M = nm;
+    for (int u = 0; u < kTPT; ++u) {
+      const int t = min(static_cast<int>(threadIdx.x) + 256 * u, p.ntile - 1);
+      st[u] = *reinterpret_cast<const float2*>(p.stat + (base + t) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      const int t = threadIdx.x + 256 * u;
+      const float mx = t < p.ntile ? st[u].x : -INFINITY, se = st[u].y;
+      hmax[u] = mx;
+      if (mx == -INFINITY) continue;
+      const float nm = fmaxf(M, mx);
+      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + se * expf(mx - nm);
+      M = nm;
+    }
   }
   for (int t = threadIdx.x + 256 * kTPT; t < p.ntile; t += 256) {
     const float mx = p.stat[(base + t) * 2], se = p.stat[(base + t) * 2 + 1];
@@ -147,19 +156,43 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   if (!fast) theta = -INFINITY;
   __syncthreads();
-  // ---- survivors: candidates >= theta of tiles whose maximum is >= theta ----
-  for (int t = threadIdx.x; t < p.ntile; t += 256) {
-    const float mx = p.stat[(base + t) * 2];
-    if (theta == -INFINITY || !(mx >= theta)) continue;
-    for (int j = 0; j < K; ++j) {
-      const float v = p.cand_val[(base + t) * K + j];
-      if (!(v >= theta)) break;
-      const int slot = atomicAdd(&nsurv, 1);
-      if (slot < kSurv) {
-        sv[slot] = v;
-        si[slot] = p.cand_id[(base + t) * K + j];
+  // ---- survivors: candidates >= theta of tiles whose maximum is >= theta.
+  // The surviving tiles are listed in LDS first (from the maxima still in
+  // registers), then one thread per (tile, rank) reads one candidate, so all
+  // of them arrive in one memory round trip ----
+  if (fast && theta != -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      const int t = threadIdx.x + 256 * u;
+      if (t < p.ntile && hmax[u] >= theta) {
+        const int slot = atomicAdd(&ntl, 1);
+        if (slot < kSurv) stile[slot] = t;
       }
     }
+  }
+  __syncthreads();
+  const int nt = ntl;
+  if (fast && theta != -INFINITY && nt <= kSurv && nt * K <= 4 * 256) {
+    float cv[4];
+    int ci[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = min(static_cast<int>(threadIdx.x) + 256 * k, nt * K - 1);
+      const int64_t at = (base + stile[idx / K]) * K + idx % K;
+      cv[k] = p.cand_val[at];
+      ci[k] = p.cand_id[at];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (static_cast<int>(threadIdx.x) + 256 * k < nt * K && cv[k] >= theta) {
+        const int slot = atomicAdd(&nsurv, 1);
+        if (slot < kSurv) {
+          sv[slot] = cv[k];
+          si[slot] = ci[k];
+        }
+      }
+  } else if (threadIdx.x == 0) {
+    nsurv = kSurv + 1;   // too many tied tiles: scan every candidate
   }
   __syncthreads();
   const int n = nsurv;
@@ -581,10 +614,26 @@ __device__ __forceinline__ float wexp(float l, float m, float T) {
   return expf((l - m) / T);
 }
 
-__global__ __launch_bounds__(256) void row_stats_kernel(VerifyParams p) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  __shared__ double sd[256];
+// Statistics of one target row (max, first index of the max, sum of
+// exp((l - max) / T) in double, non-finite flag) by one workgroup of 1024
+// threads.  When the rows are whole 16-byte vectors (V a multiple of 4, the
+// logits 16-byte aligned) and one row is at most 32768 long, every thread
+// loads its 32 values at once -- one memory round trip -- and keeps them in
+// registers for the sum; otherwise it strides over the row and reads it
+// twice.
+constexpr int kStatThreads = 1024;
+constexpr int kStatVec = 8;   // 16-byte loads per thread in the one-round path
+
+__device__ __forceinline__ void stat_take(float v, int i, float& bv, int& bi, bool& bad) {
+  if (!isfinite(v)) bad = true;
+  if (better(v, i, bv, bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(kStatThreads) void row_stats_kernel(VerifyParams p) {
+  constexpr int NW = kStatThreads / 64;
+  __shared__ float sv[NW];
+  __shared__ int si[NW];
+  __shared__ double sd[NW];
   __shared__ int sbad;
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = p.t_n[b];
@@ -592,42 +641,73 @@ __global__ __launch_bounds__(256) void row_stats_kernel(VerifyParams p) {
   const int rows1 = p.N + 1;
   const int64_t o = static_cast<int64_t>(b) * rows1 + r;
   const float* lg = p.logits + o * p.V;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) sbad = 0;
+  const bool one_round = p.V % 4 == 0 && p.V <= kStatThreads * 4 * kStatVec &&
+                         (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
+  f32x4 x[kStatVec];
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   bool bad = false;
-  for (int i = tid; i < p.V; i += 256) {
-    const float v = lg[i];
-    if (!isfinite(v)) bad = true;
-    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  if (one_round) {
+#pragma unroll
+    for (int u = 0; u < kStatVec; ++u) {
+      const int i = 4 * (tid + kStatThreads * u);
+      x[u] = i < p.V ? *reinterpret_cast<const f32x4*>(lg + i)
+                     : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int u = 0; u < kStatVec; ++u) {
+      const int i = 4 * (tid + kStatThreads * u);
+      if (i < p.V)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stat_take(x[u][e], i + e, bv, bi, bad);
+    }
+  } else {
+    for (int i = tid; i < p.V; i += kStatThreads) stat_take(lg[i], i, bv, bi, bad);
   }
-  sv[tid] = bv;
-  si[tid] = bi;
+  // block argmax (value, then the smaller index)
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = shfl_xor(bv, m);
+    const int oi = shfl_xor(bi, m);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
   __syncthreads();
   if (bad) atomicOr(&sbad, 1);
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (tid < w && better(sv[tid + w], si[tid + w], sv[tid], si[tid])) {
-      sv[tid] = sv[tid + w];
-      si[tid] = si[tid + w];
-    }
-    __syncthreads();
-  }
-  const float mx = sv[0];
+  if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+  __syncthreads();
+  float mx = sv[0];
+  int arg = si[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w)
+    if (better(sv[w], si[w], mx, arg)) { mx = sv[w]; arg = si[w]; }
+  double acc = 0.0;
   if (p.T > 0.f) {
-    double acc = 0.0;
-    for (int i = tid; i < p.V; i += 256) acc += static_cast<double>(wexp(lg[i], mx, p.T));
-    sd[tid] = acc;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (tid < w) sd[tid] += sd[tid + w];
-      __syncthreads();
+    if (one_round) {
+#pragma unroll
+      for (int u = 0; u < kStatVec; ++u) {
+        const int i = 4 * (tid + kStatThreads * u);
+        if (i < p.V)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc += static_cast<double>(wexp(x[u][e], mx, p.T));
+      }
+    } else {
+      for (int i = tid; i < p.V; i += kStatThreads) acc += static_cast<double>(wexp(lg[i], mx, p.T));
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (lane == 0) sd[wave] = acc;
+    __syncthreads();
   }
   if (tid == 0) {
+    double S = 0.0;
+    if (p.T > 0.f)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) S += sd[w];
     p.row_max[o] = mx;
-    p.row_arg[o] = si[0];
-    p.row_sum[o] = p.T > 0.f ? sd[0] : 0.0;
+    p.row_arg[o] = arg;
+    p.row_sum[o] = S;
     p.row_bad[o] = sbad;
   }
 }
@@ -1097,7 +1177,7 @@ __global__ __launch_bounds__(256) void walk_kernel(VerifyParams p) {
 }
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(row_stats_kernel, dim3(p.N + 1, p.batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(row_stats_kernel, dim3(p.N + 1, p.batch), dim3(kStatThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = static_cast<size_t>(p.D) * p.hd * p.elem_bytes;

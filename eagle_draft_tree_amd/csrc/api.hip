@@ -360,7 +360,7 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
     // splits: about 8192 waves over the batch (each keeps only one 32-key
     // step of K and V in flight), at least 64 keys each
     const int G = cf.n_q_heads / cf.n_kv_heads;
-    const int nqg = ((r.rps * G + 15) / 16 + 1) / 2;
+    const int nqg = ((r.rps * G + 15) / 16 + kAttnQBlocks - 1) / kAttnQBlocks;
     const int want = std::max(1, 8192 / std::max(1, r.batch * cf.n_kv_heads * nqg));
     int nsplit = std::min({scr.max_split, std::max(1, (kv->cap + 63) / 64), want});
     const int split_keys = std::max(64, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);

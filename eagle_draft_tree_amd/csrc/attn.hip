@@ -26,7 +26,7 @@ namespace eagle {
 
 namespace {
 
-constexpr int QBW = 2;   // 16-query blocks per wave
+constexpr int QBW = kAttnQBlocks;   // 16-query blocks per wave
 
 // 4 consecutive elements of T into half of a fragment
 template <typename T>
@@ -62,14 +62,47 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
   const int split = item / nqg, qgrp = item % nqg;
   const bool scratch = split == p.nsplit;
   const int row0 = b * p.rows_per_seq;
+  const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
+  const T* kc = static_cast<const T*>(p.kc) + bk * p.cap * HD;
+  const T* vt = static_cast<const T*>(p.vc) + bk * HD * p.cap;
+
+  // Fragments of a prefix step at t0: K rows as MFMA A fragments (lane
+  // (g, c) = key kb*16 + c) and V^T fragments (dim nb*16 + c, keys {4g + i}
+  // in elements 0..3 and {16 + 4g + i} in 4..7, as two 4-key runs --
+  // contiguous and 8-byte aligned, cap being a multiple of 8).  Rows past
+  // the cache read its last row / run; nothing here depends on which keys
+  // are live (dead keys' scores are masked and their V zeroed when the step
+  // is used), so the loads can go out before the rows' lengths are known,
+  // and every lane issues the same loads.
+  auto load_prefix = [&](int t0, Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int ci = min(t0 + kb * 16 + c, p.cap - 1);
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+        kf[kb][e].load_nt(kc + static_cast<int64_t>(ci) * HD + g * (HD / 4) + 8 * e);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int vo = min(t0 + 16 * half + 4 * g, p.cap - 4);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        load4<T>(vt + static_cast<int64_t>(nb * 16 + c) * p.cap + vo, vf[nb], half);
+    }
+  };
 
   // keys any row of this sequence may see: lane i reads row i, then a wave
   // reduction (rows_per_seq <= 64)
   int kmax = 0;
   uint64_t umask = 0;
-  if (lane < p.rows_per_seq && p.tok[row0 + lane] >= 0) {
-    kmax = min(p.plen[row0 + lane], p.cap);
-    umask = p.smask[row0 + lane];
+  {
+    // loaded together (row clamped), then selected
+    const int lr = row0 + min(lane, p.rows_per_seq - 1);
+    const int tk = p.tok[lr], pl = p.plen[lr];
+    const uint64_t sm = p.smask[lr];
+    const bool live = lane < p.rows_per_seq && tk >= 0;
+    kmax = live ? min(pl, p.cap) : 0;
+    umask = live ? sm : 0ull;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -79,9 +112,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
     const uint32_t ohi = static_cast<uint32_t>(shfl_xor(static_cast<int>(hi), o));
     umask |= (static_cast<uint64_t>(ohi) << 32) | olo;
   }
-  kmax = __shfl(kmax, 0, 64);
-  umask = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(umask >> 32), 0, 64))) << 32) |
-          static_cast<uint32_t>(__shfl(static_cast<int>(umask), 0, 64));
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  umask = (static_cast<uint64_t>(static_cast<uint32_t>(
+               __builtin_amdgcn_readfirstlane(static_cast<int>(umask >> 32)))) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(umask)));
   const int sbase = p.sbase[b];
   int kbeg, kend;
   if (scratch) {
@@ -93,8 +127,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
     kend = min(kbeg + p.split_keys, kmax);
   }
 
-  // query fragments and per-column state
-  Frag8<T> qf[QBW][NE];
+  // per-column state; queries past the sequence's live rows are zero
   f32x4 oacc[QBW][NB];
   float mrun[QBW], lrun[QBW];
   bool qok[QBW];
@@ -104,85 +137,78 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
   for (int u = 0; u < QBW; ++u) {
     const int mb = qgrp * QBW + u;
     const int m = mb * 16 + c;
-    const int i = m / G;
-    const int row = row0 + min(i, p.rows_per_seq - 1);
-    qok[u] = mb < nqb && m < QG && p.tok[row] >= 0;
-    plen_c[u] = qok[u] ? min(p.plen[row], p.cap) : 0;
-    mask_c[u] = qok[u] ? p.smask[row] : 0ull;
+    const int row = row0 + min(m / G, p.rows_per_seq - 1);
+    const int tk = p.tok[row], pl = p.plen[row];
+    const uint64_t sm = p.smask[row];
+    qok[u] = mb < nqb && m < QG && tk >= 0;
+    plen_c[u] = qok[u] ? min(pl, p.cap) : 0;
+    mask_c[u] = qok[u] ? sm : 0ull;
     mrun[u] = -INFINITY;
     lrun[u] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) oacc[u][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int head = kvh * G + m % G;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      if (qok[u])
-        qf[u][e].load(static_cast<const T*>(p.q) + (static_cast<int64_t>(row) * p.nq + head) * HD +
-                      g * (HD / 4) + 8 * e);
-      else
-        qf[u][e].zero();
-    }
   }
 
-  const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
-  const T* kc = static_cast<const T*>(p.kc) + bk * p.cap * HD;
-  const T* vt = static_cast<const T*>(p.vc) + bk * HD * p.cap;
+  // the query fragments (rows clamped into the sequence; the scores of
+  // queries past its live rows are masked), then a prefix split's first two
+  // steps
+  Frag8<T> qf[QBW][NE];
+#pragma unroll
+  for (int u = 0; u < QBW; ++u) {
+    const int m = (qgrp * QBW + u) * 16 + c;
+    const int row = row0 + min(m / G, p.rows_per_seq - 1);
+    const int head = kvh * G + m % G;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      qf[u][e].load(static_cast<const T*>(p.q) + (static_cast<int64_t>(row) * p.nq + head) * HD +
+                    g * (HD / 4) + 8 * e);
+  }
+  Frag8<T> ka[2][NE], va[NB], kb2[2][NE], vb2[NB];
+  if (!scratch && kbeg < kend) {
+    load_prefix(kbeg, ka, va);
+    load_prefix(kbeg + 32, kb2, vb2);
+  }
 
-  // 32-key steps: K fragments (two 16-key blocks) and V^T fragments of the
-  // same keys, then the online-softmax update of every query block
-  for (int t0 = kbeg; t0 < kend; t0 += 32) {
-    // cache index of step key j (0..31) and whether any query may see it
-    auto key_index = [&](int j) { return scratch ? sbase + t0 + j : t0 + j; };
-    auto key_live = [&](int j) {
-      if (scratch) return ((umask >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
-      return t0 + j < kend;
-    };
-    // ---- K fragments (A operand): lane (g, c) = key kb*16 + c ----
-    Frag8<T> kf[2][NE];
+  // cache index of key j (0..31) of the step at t0, and whether any query
+  // may see it
+  auto key_index = [&](int t0, int j) { return scratch ? sbase + t0 + j : t0 + j; };
+  auto key_live = [&](int t0, int j) {
+    if (scratch) return ((umask >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
+    return t0 + j < kend;
+  };
+
+  // Fragments of a scratch step (the tree's own rows: slots start at an
+  // arbitrary row, so V is read element by element; dead keys read zero)
+  auto load_scratch = [&](int t0, Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int j = kb * 16 + c;
-      const int ci = key_live(j) ? key_index(j) : (scratch ? 0 : t0);
+      const int ci = key_live(t0, j) ? key_index(t0, j) : 0;
 #pragma unroll
       for (int e = 0; e < NE; ++e)
         kf[kb][e].load_nt(kc + static_cast<int64_t>(ci) * HD + g * (HD / 4) + 8 * e);
     }
-    // ---- V^T fragments (A operand of O^T = V^T P^T): dim nb*16 + c, keys
-    // {4g + i} (elements 0..3) and {16 + 4g + i} (4..7); dead keys read as
-    // zero.  In a prefix step the four keys of a half are contiguous and
-    // 8-byte aligned (cap is a multiple of 8); scratch slots start at an
-    // arbitrary row and are read one by one ----
-    Frag8<T> vf[NB];
-    if (!scratch) {
-      // a prefix run of 4 keys starting below cap is readable (cap is a
-      // multiple of 8); keys past kend are zeroed after the load
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int j0 = 16 * half + 4 * g;
-        const bool inb = t0 + j0 < p.cap;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int d = nb * 16 + c;
-          if (inb) load4<T>(vt + static_cast<int64_t>(d) * p.cap + t0 + j0, vf[nb], half);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!inb || !key_live(j0 + i)) vf[nb].set(4 * half + i, 0.f);
-        }
-      }
-    } else {
-      // scratch slots start at an arbitrary row: element by element
-      for (int nb = 0; nb < NB; ++nb) {
-        const int d = nb * 16 + c;
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int j = 16 * (e8 >> 2) + 4 * g + (e8 & 3);
-          const float x = key_live(j)
-                              ? Elem<T>::to_f(vt[static_cast<int64_t>(d) * p.cap + key_index(j)])
-                              : 0.f;
-          vf[nb].set(e8, x);
-        }
+    for (int nb = 0; nb < NB; ++nb) {
+      const int d = nb * 16 + c;
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int j = 16 * (e8 >> 2) + 4 * g + (e8 & 3);
+        const float x = key_live(t0, j)
+                            ? Elem<T>::to_f(vt[static_cast<int64_t>(d) * p.cap + key_index(t0, j)])
+                            : 0.f;
+        vf[nb].set(e8, x);
       }
     }
+  };
 
+  // The online-softmax update of every query block with the step at t0.
+  auto compute = [&](int t0, const Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
+    // dead keys' V is zero (their probabilities are zero, and the rows they
+    // were read from may hold anything)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8)
+        if (!key_live(t0, 16 * (e8 >> 2) + 4 * g + (e8 & 3))) vf[nb].set(e8, 0.f);
 #pragma unroll
     for (int u = 0; u < QBW; ++u) {
       if (qgrp * QBW + u >= nqb) continue;
@@ -250,6 +276,26 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
         oacc[u][nb] = mfma16(vf[nb], ph, oacc[u][nb]);
         if constexpr (sizeof(T) == 2) oacc[u][nb] = mfma16(vf[nb], pl, oacc[u][nb]);
       }
+    }
+  };
+
+  if (!scratch) {
+    // prefix keys: each step's successor is in flight while it is used (two
+    // register sets); loads past the range re-read the cache's last rows, so
+    // every wait counts the same loads behind it
+    for (int t0 = kbeg; t0 < kend; t0 += 64) {
+      compute(t0, ka, va);
+      if (t0 + 32 >= kend) break;
+      load_prefix(t0 + 64, ka, va);
+      compute(t0 + 32, kb2, vb2);
+      if (t0 + 64 >= kend) break;
+      load_prefix(t0 + 96, kb2, vb2);
+    }
+  } else {
+    for (int t0 = kbeg; t0 < kend; t0 += 32) {
+      Frag8<T> kf[2][NE], vf[NB];
+      load_scratch(t0, kf, vf);
+      compute(t0, kf, vf);
     }
   }
 

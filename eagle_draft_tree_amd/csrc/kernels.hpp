@@ -86,6 +86,10 @@ template <typename T> hipError_t launch_pack(const GemmParams& p, void* dst, hip
 template <typename T> hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // tree attention --------------------------------------------------------------
+// 16-query blocks of one tree-attention wave (more blocks per wave share
+// the K/V loads but need more registers)
+constexpr int kAttnQBlocks = 1;
+
 struct AttnParams {
   int batch = 0, rows_per_seq = 0;
   int nq = 0, nkv = 0, hd = 0, cap = 0;

@@ -93,11 +93,28 @@ __device__ __forceinline__ void row_factors(const GemmParams& p, float* rn, int 
     return;
   }
   constexpr int TPR = 256 / (16 * MT);  // threads per row: 16, 8, 4
+  constexpr int kU = 16;                 // 16-byte loads in flight per thread
   const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
   const int row = m0 + r;
   float q = 0.f;
-  if (row < p.M)
-    for (int t = part; t < sg.ss_tiles; t += TPR) q += sg.ss[static_cast<int64_t>(row) * sg.ss_tiles + t];
+  if (row < p.M) {
+    const float* src = sg.ss + static_cast<int64_t>(row) * sg.ss_tiles;
+    if ((sg.ss_tiles & 3) == 0) {
+      // four partial sums per load, kU loads issued before any is added
+      const int n4 = sg.ss_tiles >> 2;
+      for (int t0 = part; t0 < n4; t0 += TPR * kU) {
+        f32x4 x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          x[u] = *reinterpret_cast<const f32x4*>(src + 4 * min(t0 + u * TPR, n4 - 1));
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (t0 + u * TPR < n4) q += (x[u][0] + x[u][1]) + (x[u][2] + x[u][3]);
+      }
+    } else {
+      for (int t = part; t < sg.ss_tiles; t += TPR) q += src[t];
+    }
+  }
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) q += shfl_xor(q, o);
   if (part == 0) rn[r] = 1.f / sqrtf(q / static_cast<float>(sg.width) + p.eps);
@@ -150,6 +167,42 @@ __device__ __forceinline__ void a_values(const GemmParams& p, const float* rn, i
     gv.load(static_cast<const T*>(s0.gain) + kk);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = v[i] * f * gv.get(i);
+  }
+}
+
+// A[row][k .. k+7] as stored (gathered through the segment's row index),
+// before any RMSNorm; zero past M, kend or a gather out of range
+template <typename T>
+__device__ __forceinline__ void a_raw_values(const GemmParams& p, int row, int k, int kend,
+                                             float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  if (row >= p.M || k >= kend) return;
+  const ASeg &s0 = p.seg[0], &s1 = p.seg[1], &s2 = p.seg[2];
+  const int w0 = s0.width, w01 = s0.width + s1.width;
+  const int si = (p.nseg > 1 && k >= w0) ? ((p.nseg > 2 && k >= w01) ? 2 : 1) : 0;
+  const int kk = k - (si == 0 ? 0 : (si == 1 ? w0 : w01));
+  const void* base = si == 0 ? s0.base : (si == 1 ? s1.base : s2.base);
+  const int64_t ld = si == 0 ? s0.ld : (si == 1 ? s1.ld : s2.ld);
+  const int32_t* rowidx = si == 0 ? s0.rowidx : (si == 1 ? s1.rowidx : s2.rowidx);
+  const int rowlimit = si == 0 ? s0.rowlimit : (si == 1 ? s1.rowlimit : s2.rowlimit);
+  const int f32 = si == 0 ? s0.f32 : (si == 1 ? s1.f32 : s2.f32);
+  int r = row;
+  if (rowidx != nullptr) {
+    r = rowidx[row];
+    if (r < 0 || r >= rowlimit) return;
+  }
+  if (f32) {
+    const float* src = static_cast<const float*>(base) + r * ld + kk;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
+  } else {
+    Frag8<T> w;
+    w.load(static_cast<const T*>(base) + r * ld + kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = w.get(i);
   }
 }
 
@@ -746,29 +799,47 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmParams p) {
 // a column block are numbered so that they land on the same XCD (dispatch
 // goes round-robin over the 8 XCDs) and reuse its L2 copy of the weights.
 // ============================================================================
-constexpr int kPackASteps = 4;           // k steps of A per pack_a workgroup
 constexpr int kDenseABytes = 16 * kBlk;  // A bytes of one step of a 64-row block
 
+// One 128-wide k step of a 64-row block per workgroup: each thread takes
+// four 8-element groups (rows tid / 16 + 16 i, columns 8 (tid % 16)).  The
+// values and the gain are requested first, the row factors (from the
+// producer's partial sums of squares) meanwhile, so a workgroup waits for
+// memory about once.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_a_kernel(GemmParams p) {
   __shared__ float rn[64];
   const int m0 = blockIdx.x * 64;
+  const int ksteps = (p.K + kStep - 1) / kStep;
+  const int s = blockIdx.y;
+  const int k8 = threadIdx.x & 15;
+  const int g = k8 >> 2, e = k8 & 3;
+  const int k = (s * 16 + k8) * 8;
+  const ASeg& s0 = p.seg[0];
+  const bool norm = s0.f32 && s0.ss != nullptr && k < s0.width && k < p.K;
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (threadIdx.x >> 4) + 16 * i;
+    a_raw_values<T>(p, m0 + m, k, p.K, v[i]);
+  }
+  Frag8<T> gv;
+  if (norm) gv.load(static_cast<const T*>(s0.gain) + k);
   row_factors<4>(p, rn, m0);
   __syncthreads();
-  const int ksteps = (p.K + kStep - 1) / kStep;
-  const int s0 = blockIdx.y * kPackASteps;
-  const int k8n = min(kPackASteps, ksteps - s0) * 16;
   unsigned char* out = static_cast<unsigned char*>(p.apack);
-  for (int idx = threadIdx.x; idx < 64 * k8n; idx += 256) {
-    const int m = idx / k8n, k8 = idx - m * k8n;
-    float v[8];
-    a_values<T>(p, rn, m, m0 + m, (s0 * 16 + k8) * 8, p.K, v);
-    const int s = s0 + (k8 >> 4), rem = k8 & 15;
-    const int g = rem >> 2, e = rem & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (threadIdx.x >> 4) + 16 * i;
+    if (norm) {
+      const float f = rn[m];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * f * gv.get(j);
+    }
     const int rt = (m0 >> 4) + (m >> 4), c = m & 15;
     unsigned char* blk = out + ((static_cast<int64_t>(rt) * ksteps + s) * 4 + e) * kBlk;
     u32x4 hi, lo;
-    split_hi_lo(v, hi, lo);
+    split_hi_lo(v[i], hi, lo);
     *reinterpret_cast<u32x4*>(blk + (g * 16 + c) * 16) = hi;
     *reinterpret_cast<u32x4*>(blk + 1024 + (g * 16 + c) * 16) = lo;
   }
@@ -1011,8 +1082,7 @@ hipError_t launch_dense(const GemmParams& p, hipStream_t s) {
   } else {
     const int RB = (p.M + 63) / 64;
     const int ksteps = (p.K + kStep - 1) / kStep;
-    hipLaunchKernelGGL(pack_a_kernel<T>, dim3(RB, (ksteps + kPackASteps - 1) / kPackASteps),
-                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL(pack_a_kernel<T>, dim3(RB, ksteps), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ngroups = (p.N / 16 + 15) / 16;

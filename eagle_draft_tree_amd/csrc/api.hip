@@ -357,11 +357,11 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
     p.q = scr.q; p.o = reinterpret_cast<float*>(scr.o);
     p.kc = kv->k; p.vc = kv->v; p.tok = r.tok; p.plen = r.plen;
     p.sbase = r.sbase; p.smask = r.mask;
-    // splits: about 8192 waves over the batch (each keeps only one 32-key
-    // step of K and V in flight), at least 64 keys each
+    // splits: about 2048 workgroups over the batch (each stages 32-key
+    // steps of K and V for up to four 16-query blocks), at least 64 keys each
     const int G = cf.n_q_heads / cf.n_kv_heads;
-    const int nqg = ((r.rps * G + 15) / 16 + kAttnQBlocks - 1) / kAttnQBlocks;
-    const int want = std::max(1, 8192 / std::max(1, r.batch * cf.n_kv_heads * nqg));
+    const int nrounds = ((r.rps * G + 15) / 16 + 3) / 4;
+    const int want = std::max(1, 2048 / std::max(1, r.batch * cf.n_kv_heads * nrounds));
     int nsplit = std::min({scr.max_split, std::max(1, (kv->cap + 63) / 64), want});
     const int split_keys = std::max(64, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);
     nsplit = (kv->cap + split_keys - 1) / split_keys;

@@ -1,13 +1,17 @@
 // Tree attention of the draft layer (split-KV, "flash decoding" style).
 //
-// The query vectors of a sequence that share a kv head (rows_per_seq rows x
-// G grouped heads, at most 128) are the MFMA columns.  Every wave owns one
-// key range (a split) and up to QBW blocks of 16 query vectors, and runs the
-// online softmax over its keys with the state in registers:
-//  * S^T = K Q^T: K rows are read straight from the cache as MFMA A
-//    fragments (lane (g, c): key c, 32 contiguous dims), Q as B fragments
-//    with the same dim permutation; lane (g, c) ends up holding keys
-//    4g + i of query column c;
+// One workgroup per (key range = split, kv head, sequence, round of four
+// 16-query blocks).  The query vectors of a sequence that share a kv head
+// (rows_per_seq rows x G grouped heads) are the MFMA columns; each of the
+// four waves owns one block of 16 of them and runs the online softmax over
+// the split's keys with its state in registers.  The keys are visited 32 at
+// a time: the workgroup stages each step's K rows and V^T columns in LDS
+// (double-buffered, the loads of the step after next in flight in
+// registers), so every K/V byte is read from memory once per workgroup and
+// shared by its query blocks.
+//  * S^T = K Q^T: lane (g, c) reads key c's 8-dim fragments from the staged
+//    K tile as the MFMA A operand, Q as the B operand with the same dim
+//    permutation; it ends up holding keys 4g + i of query column c;
 //  * O^T += V^T P^T: the V cache is stored transposed ([hd, cap] per head),
 //    so lane (g, c) reads its 8 keys of dim c as two 4-key runs -- exactly
 //    the keys whose probabilities it already holds, which makes them the B
@@ -16,7 +20,6 @@
 //  * visibility: cache rows [0, prefix_len) of the query's row (prefix
 //    splits) and scratch rows scratch_base + j for the set bits j of the
 //    row's 64-bit ancestor mask (the last split).
-// Keys are visited 32 at a time, which keeps a wave within 256 registers.
 // Each wave writes its (max, sum, O) per query vector; a second kernel
 // merges the splits in split order.  No workgroup waits on another.
 #include "common.hpp"
@@ -26,77 +29,81 @@ namespace eagle {
 
 namespace {
 
-constexpr int QBW = kAttnQBlocks;   // 16-query blocks per wave
-
-// 4 consecutive elements of T into half of a fragment
+// 16 bytes of LDS as 8 (bf16) or 4 (fp32) elements into a fragment
 template <typename T>
-__device__ __forceinline__ void load4(const T* p, Frag8<T>& f, int half);
+__device__ __forceinline__ void lds_frag8(const unsigned char* p, Frag8<T>& f);
 template <>
-__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, Frag8<uint16_t>& f, int half) {
+__device__ __forceinline__ void lds_frag8<uint16_t>(const unsigned char* p, Frag8<uint16_t>& f) {
+  f.v = *reinterpret_cast<const u32x4*>(p);
+}
+template <>
+__device__ __forceinline__ void lds_frag8<float>(const unsigned char* p, Frag8<float>& f) {
+  f.a = *reinterpret_cast<const f32x4*>(p);
+  f.b = *reinterpret_cast<const f32x4*>(p + 16);
+}
+// 4 consecutive elements of LDS into half of a fragment
+template <typename T>
+__device__ __forceinline__ void lds_half4(const unsigned char* p, Frag8<T>& f, int half);
+template <>
+__device__ __forceinline__ void lds_half4<uint16_t>(const unsigned char* p, Frag8<uint16_t>& f,
+                                                    int half) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
   f.v[2 * half] = v.x;
   f.v[2 * half + 1] = v.y;
 }
 template <>
-__device__ __forceinline__ void load4<float>(const float* p, Frag8<float>& f, int half) {
+__device__ __forceinline__ void lds_half4<float>(const unsigned char* p, Frag8<float>& f, int half) {
   const f32x4 v = *reinterpret_cast<const f32x4*>(p);
   if (half == 0) f.a = v; else f.b = v;
 }
 
 }  // namespace
 
+// LDS layout of one staged step: K tile [32 keys][HD] then V^T tile
+// [HD][32 keys], rows padded (16 and 8/16 bytes) so that the 16 lanes
+// reading 16 keys (K) or 16 dims (V^T) hit distinct banks.
 template <typename T, int HD>
-__global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
+struct AttnTile {
+  static constexpr int E = 16 / sizeof(T);                  // elements per 16 B
+  static constexpr int KSTR = HD * sizeof(T) + 16;
+  static constexpr int VSTR = 32 * sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
+  static constexpr int KCH = HD * sizeof(T) / 16;           // 16-byte chunks per K row
+  static constexpr int VCH = 32 * sizeof(T) / 16;           // per V^T row
+  static constexpr int NKC = 32 * KCH;                      // K chunks per step
+  static constexpr int NCH = NKC + HD * VCH;                // all chunks per step
+  static constexpr int CPT = NCH / 256;                     // chunks per thread
+  static constexpr int BUF = 32 * KSTR + HD * VSTR;         // bytes per buffer
+  static_assert(NKC % 256 == 0 && NCH % 256 == 0, "chunks split evenly over 256 threads");
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
+  using L = AttnTile<T, HD>;
   constexpr int NE = HD / 32;   // 8-element fragments per lane per query / key
   constexpr int NB = HD / 16;   // 16-dim blocks of O^T
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * L::BUF];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int kvh = blockIdx.y, b = blockIdx.z;
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
   const int nqb = (QG + 15) / 16;
-  const int nqg = (nqb + QBW - 1) / QBW;
-  const int NS = p.nsplit + 1;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= NS * nqg) return;
-  const int split = item / nqg, qgrp = item % nqg;
+  const int nrounds = (nqb + 3) / 4;
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int b = blockIdx.z / nrounds, round = blockIdx.z % nrounds;
+  const int qb = round * 4 + wave;   // this wave's query block (none past nqb)
+  const bool active = qb < nqb;
   const bool scratch = split == p.nsplit;
   const int row0 = b * p.rows_per_seq;
   const int64_t bk = static_cast<int64_t>(b) * p.nkv + kvh;
   const T* kc = static_cast<const T*>(p.kc) + bk * p.cap * HD;
   const T* vt = static_cast<const T*>(p.vc) + bk * HD * p.cap;
 
-  // Fragments of a prefix step at t0: K rows as MFMA A fragments (lane
-  // (g, c) = key kb*16 + c) and V^T fragments (dim nb*16 + c, keys {4g + i}
-  // in elements 0..3 and {16 + 4g + i} in 4..7, as two 4-key runs --
-  // contiguous and 8-byte aligned, cap being a multiple of 8).  Rows past
-  // the cache read its last row / run; nothing here depends on which keys
-  // are live (dead keys' scores are masked and their V zeroed when the step
-  // is used), so the loads can go out before the rows' lengths are known,
-  // and every lane issues the same loads.
-  auto load_prefix = [&](int t0, Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int ci = min(t0 + kb * 16 + c, p.cap - 1);
-#pragma unroll
-      for (int e = 0; e < NE; ++e)
-        kf[kb][e].load_nt(kc + static_cast<int64_t>(ci) * HD + g * (HD / 4) + 8 * e);
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int vo = min(t0 + 16 * half + 4 * g, p.cap - 4);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        load4<T>(vt + static_cast<int64_t>(nb * 16 + c) * p.cap + vo, vf[nb], half);
-    }
-  };
-
-  // keys any row of this sequence may see: lane i reads row i, then a wave
-  // reduction (rows_per_seq <= 64)
+  // keys any row of this sequence may see (the same in every wave): lane i
+  // reads row i, then a wave reduction (rows_per_seq <= 64)
   int kmax = 0;
   uint64_t umask = 0;
   {
-    // loaded together (row clamped), then selected
     const int lr = row0 + min(lane, p.rows_per_seq - 1);
     const int tk = p.tok[lr], pl = p.plen[lr];
     const uint64_t sm = p.smask[lr];
@@ -127,46 +134,30 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
     kend = min(kbeg + p.split_keys, kmax);
   }
 
-  // per-column state; queries past the sequence's live rows are zero
-  f32x4 oacc[QBW][NB];
-  float mrun[QBW], lrun[QBW];
-  bool qok[QBW];
-  int plen_c[QBW];
-  uint64_t mask_c[QBW];
-#pragma unroll
-  for (int u = 0; u < QBW; ++u) {
-    const int mb = qgrp * QBW + u;
-    const int m = mb * 16 + c;
-    const int row = row0 + min(m / G, p.rows_per_seq - 1);
-    const int tk = p.tok[row], pl = p.plen[row];
-    const uint64_t sm = p.smask[row];
-    qok[u] = mb < nqb && m < QG && tk >= 0;
-    plen_c[u] = qok[u] ? min(pl, p.cap) : 0;
-    mask_c[u] = qok[u] ? sm : 0ull;
-    mrun[u] = -INFINITY;
-    lrun[u] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) oacc[u][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this wave's query column: row, head, visibility, online-softmax state
+  const int m = qb * 16 + c;
+  const int qrow = row0 + min(m / G, p.rows_per_seq - 1);
+  bool qok;
+  int plen_c;
+  uint64_t mask_c;
+  {
+    const int tk = p.tok[qrow], pl = p.plen[qrow];
+    const uint64_t sm = p.smask[qrow];
+    qok = active && m < QG && tk >= 0;
+    plen_c = qok ? min(pl, p.cap) : 0;
+    mask_c = qok ? sm : 0ull;
   }
-
-  // the query fragments (rows clamped into the sequence; the scores of
-  // queries past its live rows are masked), then a prefix split's first two
-  // steps
-  Frag8<T> qf[QBW][NE];
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 oacc[NB];
 #pragma unroll
-  for (int u = 0; u < QBW; ++u) {
-    const int m = (qgrp * QBW + u) * 16 + c;
-    const int row = row0 + min(m / G, p.rows_per_seq - 1);
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frag8<T> qf[NE];
+  {
     const int head = kvh * G + m % G;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
-      qf[u][e].load(static_cast<const T*>(p.q) + (static_cast<int64_t>(row) * p.nq + head) * HD +
-                    g * (HD / 4) + 8 * e);
-  }
-  Frag8<T> ka[2][NE], va[NB], kb2[2][NE], vb2[NB];
-  if (!scratch && kbeg < kend) {
-    load_prefix(kbeg, ka, va);
-    load_prefix(kbeg + 32, kb2, vb2);
+      qf[e].load(static_cast<const T*>(p.q) + (static_cast<int64_t>(qrow) * p.nq + head) * HD +
+                 g * (HD / 4) + 8 * e);
   }
 
   // cache index of key j (0..31) of the step at t0, and whether any query
@@ -177,145 +168,182 @@ __global__ __launch_bounds__(256, 2) void tree_attn_kernel(AttnParams p) {
     return t0 + j < kend;
   };
 
-  // Fragments of a scratch step (the tree's own rows: slots start at an
-  // arbitrary row, so V is read element by element; dead keys read zero)
-  auto load_scratch = [&](int t0, Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
+  // ---- staging: thread t moves 16-byte chunks t + 256 i of a step ----
+  u32x4 stg[L::CPT];
+  // request the chunks of the step at t0 (rows past the cache read its last
+  // rows; dead keys are masked when the step is used)
+  auto fetch = [&](int t0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int j = kb * 16 + c;
-      const int ci = key_live(t0, j) ? key_index(t0, j) : 0;
+    for (int i = 0; i < L::CPT; ++i) {
+      const int q = tid + 256 * i;
+      if (i < L::NKC / 256) {
+        const int key = q / L::KCH, cc = q % L::KCH;
+        const int row = min(key_index(t0, key), p.cap - 1);
+        stg[i] = *reinterpret_cast<const u32x4*>(kc + static_cast<int64_t>(row) * HD + cc * L::E);
+      } else {
+        const int qq = q - L::NKC;
+        const int d = qq / L::VCH, cv = qq % L::VCH;
+        const T* vrow = vt + static_cast<int64_t>(d) * p.cap;
+        if (!scratch) {
+          // prefix keys: a 16-byte run (cap is a multiple of 8)
+          const int k0 = min(t0 + cv * L::E, p.cap - L::E);
+          stg[i] = *reinterpret_cast<const u32x4*>(vrow + k0);
+        } else {
+          // scratch slots start at an arbitrary row: element by element
+          u32x4 w;
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
-        kf[kb][e].load_nt(kc + static_cast<int64_t>(ci) * HD + g * (HD / 4) + 8 * e);
-    }
-    for (int nb = 0; nb < NB; ++nb) {
-      const int d = nb * 16 + c;
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int j = 16 * (e8 >> 2) + 4 * g + (e8 & 3);
-        const float x = key_live(t0, j)
-                            ? Elem<T>::to_f(vt[static_cast<int64_t>(d) * p.cap + key_index(t0, j)])
-                            : 0.f;
-        vf[nb].set(e8, x);
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (sizeof(T) == 2) {
+              const int k = sbase + t0 + cv * L::E + 2 * e;
+              const uint32_t lo = vrow[min(k, p.cap - 1)], hi = vrow[min(k + 1, p.cap - 1)];
+              w[e] = lo | (hi << 16);
+            } else {
+              w[e] = __float_as_uint(vrow[min(sbase + t0 + cv * L::E + e, p.cap - 1)]);
+            }
+          }
+          stg[i] = w;
+        }
       }
     }
   };
-
-  // The online-softmax update of every query block with the step at t0.
-  auto compute = [&](int t0, const Frag8<T> (&kf)[2][NE], Frag8<T> (&vf)[NB]) {
-    // dead keys' V is zero (their probabilities are zero, and the rows they
-    // were read from may hold anything)
+  auto put = [&](int buf) {
+    unsigned char* base = lds + buf * L::BUF;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8)
-        if (!key_live(t0, 16 * (e8 >> 2) + 4 * g + (e8 & 3))) vf[nb].set(e8, 0.f);
-#pragma unroll
-    for (int u = 0; u < QBW; ++u) {
-      if (qgrp * QBW + u >= nqb) continue;
-      // S^T block: 32 keys x 16 query columns
-      f32x4 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < NE; ++e) sc[kb] = mfma16(kf[kb][e], qf[u][e], sc[kb]);
+    for (int i = 0; i < L::CPT; ++i) {
+      const int q = tid + 256 * i;
+      unsigned char* dst;
+      if (i < L::NKC / 256) {
+        dst = base + (q / L::KCH) * L::KSTR + (q % L::KCH) * 16;
+      } else {
+        const int qq = q - L::NKC;
+        dst = base + 32 * L::KSTR + (qq / L::VCH) * L::VSTR + (qq % L::VCH) * 16;
       }
-      float tmax = -INFINITY;
+      // V^T rows are 8-byte aligned only
+      reinterpret_cast<uint2*>(dst)[0] = uint2{stg[i][0], stg[i][1]};
+      reinterpret_cast<uint2*>(dst)[1] = uint2{stg[i][2], stg[i][3]};
+    }
+  };
+
+  // The online-softmax update of this wave's query block with the staged
+  // step at t0 in buffer buf.
+  auto compute = [&](int t0, int buf) {
+    const unsigned char* kt = lds + buf * L::BUF;
+    const unsigned char* vtt = kt + 32 * L::KSTR;
+    Frag8<T> kf[2][NE];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+        lds_frag8<T>(kt + (kb * 16 + c) * L::KSTR + (g * (HD / 4) + 8 * e) * sizeof(T), kf[kb][e]);
+    Frag8<T> vf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const unsigned char* vr = vtt + (nb * 16 + c) * L::VSTR;
+      lds_half4<T>(vr + 4 * g * sizeof(T), vf[nb], 0);
+      lds_half4<T>(vr + (16 + 4 * g) * sizeof(T), vf[nb], 1);
+    }
+    // dead keys' V is zero (their probabilities are zero, and the rows they
+    // were read from may hold anything); a step of live keys skips this
+    if (!(t0 + 32 <= kend && !scratch)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8)
+          if (!key_live(t0, 16 * (e8 >> 2) + 4 * g + (e8 & 3))) vf[nb].set(e8, 0.f);
+    }
+    // S^T block: 32 keys x 16 query columns
+    f32x4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < NE; ++e) sc[kb] = mfma16(kf[kb][e], qf[e], sc[kb]);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = kb * 16 + 4 * g + i;
+        bool vis;
+        if (scratch) vis = ((mask_c >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
+        else vis = t0 + j < plen_c && t0 + j < kend;
+        vis = vis && qok;
+        const float v = vis ? sc[kb][i] * p.scale : -INFINITY;
+        sc[kb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float mnew = fmaxf(mrun, tmax);
+    float alpha = 1.f, psum = 0.f;
+    if (mnew != -INFINITY) {
+      alpha = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = kb * 16 + 4 * g + i;
-          bool vis;
-          if (scratch) vis = ((mask_c[u] >> (t0 + j)) & 1ull) != 0 && sbase + t0 + j < p.cap;
-          else vis = t0 + j < plen_c[u] && t0 + j < kend;
-          vis = vis && qok[u];
-          const float v = vis ? sc[kb][i] * p.scale : -INFINITY;
-          sc[kb][i] = v;
-          tmax = fmaxf(tmax, v);
+          const float pv = (sc[kb][i] == -INFINITY) ? 0.f : expf(sc[kb][i] - mnew);
+          sc[kb][i] = pv;
+          psum += pv;
         }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrun[u], tmax);
-      float alpha = 1.f, psum = 0.f;
-      if (mnew != -INFINITY) {
-        alpha = (mrun[u] == -INFINITY) ? 0.f : expf(mrun[u] - mnew);
+    } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    psum += shfl_xor(psum, 16);
+    psum += shfl_xor(psum, 32);
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = (sc[kb][i] == -INFINITY) ? 0.f : expf(sc[kb][i] - mnew);
-            sc[kb][i] = pv;
-            psum += pv;
-          }
-      } else {
+    for (int nb = 0; nb < NB; ++nb) oacc[nb] *= alpha;
+    // P^T fragment: the lane's own probabilities, keys {4g + i} (elements
+    // 0..3) and {16 + 4g + i} (elements 4..7)
+    Frag8<T> ph, pl;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = sc[0][i], p1 = sc[1][i];
+      ph.set(i, p0);
+      ph.set(4 + i, p1);
+      if constexpr (sizeof(T) == 2) {
+        pl.set(i, p0 - ph.get(i));
+        pl.set(4 + i, p1 - ph.get(4 + i));
       }
-      psum += shfl_xor(psum, 16);
-      psum += shfl_xor(psum, 32);
-      lrun[u] = lrun[u] * alpha + psum;
-      mrun[u] = mnew;
+    }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[u][nb] *= alpha;
-      // P^T fragment: the lane's own probabilities, keys {4g + i} (elements
-      // 0..3) and {16 + 4g + i} (elements 4..7)
-      Frag8<T> ph, pl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = sc[0][i], p1 = sc[1][i];
-        ph.set(i, p0);
-        ph.set(4 + i, p1);
-        if constexpr (sizeof(T) == 2) {
-          pl.set(i, p0 - ph.get(i));
-          pl.set(4 + i, p1 - ph.get(4 + i));
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        oacc[u][nb] = mfma16(vf[nb], ph, oacc[u][nb]);
-        if constexpr (sizeof(T) == 2) oacc[u][nb] = mfma16(vf[nb], pl, oacc[u][nb]);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      oacc[nb] = mfma16(vf[nb], ph, oacc[nb]);
+      if constexpr (sizeof(T) == 2) oacc[nb] = mfma16(vf[nb], pl, oacc[nb]);
     }
   };
 
-  if (!scratch) {
-    // prefix keys: each step's successor is in flight while it is used (two
-    // register sets); loads past the range re-read the cache's last rows, so
-    // every wait counts the same loads behind it
-    for (int t0 = kbeg; t0 < kend; t0 += 64) {
-      compute(t0, ka, va);
-      if (t0 + 32 >= kend) break;
-      load_prefix(t0 + 64, ka, va);
-      compute(t0 + 32, kb2, vb2);
-      if (t0 + 64 >= kend) break;
-      load_prefix(t0 + 96, kb2, vb2);
-    }
-  } else {
-    for (int t0 = kbeg; t0 < kend; t0 += 32) {
-      Frag8<T> kf[2][NE], vf[NB];
-      load_scratch(t0, kf, vf);
-      compute(t0, kf, vf);
+  // ---- the steps: step s + 1 is staged from registers while step s is
+  // used, and the loads of step s + 2 are in flight meanwhile ----
+  const int nst = kbeg < kend ? (kend - kbeg + 31) / 32 : 0;
+  if (nst > 0) {
+    fetch(kbeg);
+    put(0);
+    if (nst > 1) fetch(kbeg + 32);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      if (st + 1 < nst) put((st + 1) & 1);
+      if (st + 2 < nst) fetch(kbeg + 32 * (st + 2));
+      if (active) compute(kbeg + 32 * st, st & 1);
+      __syncthreads();
     }
   }
 
   // ---- this split's partial (max, sum, O) per query vector ----
+  if (!active || m >= QG) return;
   const int NSP = p.nsplit + 1;
-#pragma unroll
-  for (int u = 0; u < QBW; ++u) {
-    const int mb = qgrp * QBW + u;
-    const int m = mb * 16 + c;
-    if (mb >= nqb || m >= QG) continue;
-    const int64_t base = (bk * NSP + split) * QG + m;
-    if (g == 0) {
-      p.part_ml[base * 2] = mrun[u];
-      p.part_ml[base * 2 + 1] = lrun[u];
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.part_o[base * HD + nb * 16 + 4 * g + i] = oacc[u][nb][i];
+  const int64_t base = (bk * NSP + split) * QG + m;
+  if (g == 0) {
+    p.part_ml[base * 2] = mrun;
+    p.part_ml[base * 2 + 1] = lrun;
   }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    *reinterpret_cast<f32x4*>(p.part_o + base * HD + nb * 16 + 4 * g) = oacc[nb];
 }
 
 // Merge of the splits: one workgroup per (query vector, kv head, sequence),
@@ -380,17 +408,17 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int G = p.nq / p.nkv;
   const int QG = p.rows_per_seq * G;
   if (p.rows_per_seq > 64 || QG > 1024 || p.split_keys % 64 || p.split_keys < 64 ||
-      p.nsplit + 1 > kMergeThreads)
+      p.nsplit + 1 > kMergeThreads || p.cap % 8 || p.cap < 32)
     return hipErrorInvalidValue;
-  const int nqb = (QG + 15) / 16;
-  const int nqg = (nqb + QBW - 1) / QBW;
-  const int items = (p.nsplit + 1) * nqg;
-  dim3 grid((items + 3) / 4, p.nkv, p.batch);
+  const int nrounds = ((QG + 15) / 16 + 3) / 4;
+  dim3 grid(p.nsplit + 1, p.nkv, p.batch * nrounds);
   if constexpr (sizeof(T) == 2) {
     if (p.hd == 128)
       hipLaunchKernelGGL((tree_attn_kernel<T, 128>), grid, dim3(256), 0, s, p);
-    else
+    else if (p.hd == 64)
       hipLaunchKernelGGL((tree_attn_kernel<T, 64>), grid, dim3(256), 0, s, p);
+    else
+      return hipErrorInvalidValue;
   } else {
     // fp32 storage is supported with head_dim 64 only
     if (p.hd != 64) return hipErrorInvalidValue;

@@ -86,10 +86,6 @@ template <typename T> hipError_t launch_pack(const GemmParams& p, void* dst, hip
 template <typename T> hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // tree attention --------------------------------------------------------------
-// 16-query blocks of one tree-attention wave (more blocks per wave share
-// the K/V loads but need more registers)
-constexpr int kAttnQBlocks = 1;
-
 struct AttnParams {
   int batch = 0, rows_per_seq = 0;
   int nq = 0, nkv = 0, hd = 0, cap = 0;
@@ -103,6 +99,7 @@ struct AttnParams {
   const uint64_t* smask = nullptr;  // [rows]
   int nsplit = 1;                   // prefix splits (plus one scratch split)
   int split_keys = 64;              // keys per prefix split (multiple of 64)
+                                    // cap: a multiple of 8, at least 32
   float* part_o = nullptr;          // [B, nkv, nsplit+1, QG, hd]
   float* part_ml = nullptr;         // [B, nkv, nsplit+1, QG, 2]
   float scale = 1.f;

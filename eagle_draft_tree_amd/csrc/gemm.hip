@@ -316,6 +316,60 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
           lm[(mt * 16 + 4 * g + j) * W + (wave * CT + ct) * 16 + c] = acc[mt][ct][j];
     __syncthreads();
     const int rows = min(16 * MT, p.M - m0);
+    if constexpr (MT == 4) {
+      // many rows: one (row, tile) pair per thread, each keeping its tile's
+      // top-k in registers (a wave-wide sort per pair would take the
+      // workgroup's 64 x CT pairs one at a time per wave); the thread starts
+      // its scan at its own offset, so the threads of a wave read distinct
+      // LDS banks -- the (value, id) order does not depend on scan order
+      for (int pr = threadIdx.x; pr < 64 * CT; pr += 256) {
+        const int r = pr / CT, ch = pr % CT;
+        const int lt = group * CT + ch;
+        if (r >= rows || lt >= p.ntile_lm) continue;
+        const float* row = lm + r * W + ch * 64;
+        float lv[kMaxTopK];
+        int li[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+        float mx = -INFINITY;
+        for (int jj = 0; jj < 64; ++jj) {
+          const int j = (jj + pr) & 63;
+          const int col = lt * 64 + j;
+          float v = col < p.N ? row[j] : -INFINITY;
+          if (v != v) v = -INFINITY;
+          const int id = col < p.N ? col : 0x7fffffff;
+          mx = fmaxf(mx, v);
+          // insertion into the sorted list: slot j takes the new pair when
+          // it beats slot j but not slot j - 1, slot j - 1's pair when the
+          // new one beats that too
+          bool bt[kMaxTopK];
+#pragma unroll
+          for (int k = 0; k < kMaxTopK; ++k) bt[k] = k < p.topk && better(v, id, lv[k], li[k]);
+#pragma unroll
+          for (int k = kMaxTopK - 1; k >= 0; --k) {
+            if (k > 0 && bt[k - 1]) { lv[k] = lv[k - 1]; li[k] = li[k - 1]; }
+            else if (bt[k]) { lv[k] = v; li[k] = id; }
+          }
+        }
+        float se = 0.f;
+        for (int jj = 0; jj < 64; ++jj) {
+          const int j = (jj + pr) & 63;
+          float v = lt * 64 + j < p.N ? row[j] : -INFINITY;
+          if (v != v) v = -INFINITY;
+          se += v == -INFINITY ? 0.f : expf(v - mx);
+        }
+        const int64_t o = static_cast<int64_t>(m0 + r) * p.ntile_lm + lt;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+          if (k < p.topk) {
+            p.cand_val[o * p.topk + k] = lv[k];
+            p.cand_id[o * p.topk + k] = li[k];
+          }
+        p.stat[o * 2] = mx;
+        p.stat[o * 2 + 1] = se;
+      }
+      return;
+    }
     for (int r = wave; r < rows; r += 4) {
 #pragma unroll
       for (int ch = 0; ch < CT; ++ch) {
@@ -456,36 +510,47 @@ __device__ __forceinline__ bool splitk_last(const GemmParams& p, f32x4 (&acc)[MT
   __syncthreads();
   if (!last) return false;
   // The last workgroup sums the partials of its 16 MT x 64 CT tile in
-  // split order: each thread takes tile elements four at a time and issues
-  // all of their split loads before adding any (one memory round trip per
-  // group of four, not one per split), the sums are staged in LDS and each
-  // lane then takes its accumulators back in fragment layout.
-  constexpr int kMaxS = 16, kCh = 4;
+  // split order: each thread takes kCh tile elements and reads their
+  // partials kSB splits at a time, every load of a batch issued before any
+  // is added (addresses clamped into the buffer, so no load sits behind a
+  // branch that would make it wait on its own) -- one memory round trip per
+  // batch; the sums are staged in LDS and each lane then takes its
+  // accumulators back in fragment layout.
+  constexpr int kCh = MT >= 4 ? 16 : 4, kSB = 4;
   constexpr int rows = 16 * MT, cols = 64 * CT;
   float* red = reinterpret_cast<float*>(lds);
+  const int64_t split_stride = static_cast<int64_t>(p.Mtot) * p.N;
   for (int e0 = threadIdx.x; e0 < rows * cols; e0 += 256 * kCh) {
-    float part[kCh][kMaxS];
+    float sum[kCh];
+    int64_t off[kCh];
+    bool ok[kCh];
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
       const int e = e0 + i * 256;
       const int m = m0 + e / cols, col = group * cols + e % cols;
-      const bool ok = e < rows * cols && m < p.M && col < p.N;
-      const float* src = p.part + static_cast<int64_t>(m) * p.N + col;
+      ok[i] = e < rows * cols && m < p.M && col < p.N;
+      off[i] = ok[i] ? static_cast<int64_t>(m) * p.N + col : 0;
+      sum[i] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < p.S; sp0 += kSB) {
+      float part[kCh][kSB];
 #pragma unroll
-      for (int sp = 0; sp < kMaxS; ++sp)
-        part[i][sp] = (ok && sp < p.S)
-                          ? __hip_atomic_load(src + static_cast<int64_t>(sp) * p.Mtot * p.N,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                          : 0.f;
+      for (int i = 0; i < kCh; ++i)
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+          const int sp = min(sp0 + j, p.S - 1);
+          part[i][j] = __hip_atomic_load(p.part + sp * split_stride + off[i], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+      for (int i = 0; i < kCh; ++i)
+#pragma unroll
+        for (int j = 0; j < kSB; ++j)
+          if (sp0 + j < p.S) sum[i] += part[i][j];
     }
 #pragma unroll
-    for (int i = 0; i < kCh; ++i) {
-      const int e = e0 + i * 256;
-      float sum = 0.f;
-#pragma unroll
-      for (int sp = 0; sp < kMaxS; ++sp) sum += part[i][sp];
-      if (e < rows * cols) red[e] = sum;
-    }
+    for (int i = 0; i < kCh; ++i)
+      if (e0 + i * 256 < rows * cols) red[e0 + i * 256] = ok[i] ? sum[i] : 0.f;
   }
   __syncthreads();
 #pragma unroll
@@ -992,14 +1057,17 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int ntiles = p.N / 16;
   p.dense = !fp32 && p.M > 64 && p.apack != nullptr && p.M <= p.apack_rows;
   if (p.dense) {
-    // 64 x 256 tiles; split K until about 1.5 tiles per CU, each split
-    // keeping at least four steps, within the partial-sum buffer
+    // 64 x 256 tiles; K is split only when it is long (a split costs a
+    // round of partial sums through memory, more than a few steps of the
+    // main loop): down to about 48 steps per split, while the grid stays
+    // within two tiles per CU and the partial sums fit their buffer
     const int RB = (p.M + 63) / 64, ngroups = (ntiles + 15) / 16;
     const int ksteps = (p.K + kStep - 1) / kStep;
     int S = 1;
-    while (RB * ngroups * S < (3 * num_cus) / 2 && ksteps / (S + 1) >= 4 && S < 16 &&
-           static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
-      ++S;
+    if (ksteps > 64)
+      while (ksteps / S > 48 && RB * ngroups * (S + 1) <= 2 * num_cus && S < 16 &&
+             static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
+        ++S;
     const int steps = (ksteps + S - 1) / S;
     p.MT = 4; p.CT = 4;
     p.KS = steps * kStep;

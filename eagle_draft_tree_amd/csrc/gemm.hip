@@ -1092,7 +1092,11 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
     while (ngroups * chunks * S < 2 * num_cus && (ksteps + S) / (S + 1) >= 2 && S < 16) ++S;
   // the partial sums must fit the workspace
   while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
-  const int steps = (ksteps + S - 1) / S;
+  // a split longer than 4 steps is rounded up to whole pieces (fewer,
+  // longer splits): steps past the slice still stream their weights, against
+  // zero A, so a ragged piece costs bandwidth
+  int steps = (ksteps + S - 1) / S;
+  if (steps > 4) steps = (steps + pmax - 1) / pmax * pmax;
   p.KS = steps * kStep;
   p.S = (ksteps + steps - 1) / steps;
   // smallest unrolled piece that holds the slice (several pieces otherwise)

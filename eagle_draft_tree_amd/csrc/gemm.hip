@@ -1085,11 +1085,12 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int ksteps = (p.K + kStep - 1) / kStep;
   const int pmax = max_piece(p.MT);
   // no K split when the column groups alone cover every CU; else split K
-  // until the grid holds about two workgroups per CU, each split keeping at
-  // least two steps
+  // until the grid holds about one workgroup per CU (each split's partial
+  // sums cost a round trip through memory, so fewer, longer splits do
+  // better than more workgroups), each split keeping at least two steps
   int S = 1;
   if (ngroups * chunks < num_cus)
-    while (ngroups * chunks * S < 2 * num_cus && (ksteps + S) / (S + 1) >= 2 && S < 16) ++S;
+    while (ngroups * chunks * S < num_cus && (ksteps + S) / (S + 1) >= 2 && S < 16) ++S;
   // the partial sums must fit the workspace
   while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
   // a split longer than 4 steps is rounded up to whole pieces (fewer,

@@ -35,7 +35,7 @@ struct Layout {
 };
 
 struct Offsets {
-  size_t x, h, a0, a1, q, o, t, ss, part, lm_val, lm_id,
+  size_t x, h, a0, a1, q, o, t, ss, part, lm_logits,
       lm_stat, tk_id, tk_val, lse, at_o, at_ml, desc[2][7], sbase, c_token,
       c_parent, c_slot, c_row, c_score, c_mask, c_depth, n_cand, p_root,
       len_out, v_max, v_sum, v_arg, v_bad, status, counters_begin, counters_end,
@@ -133,8 +133,7 @@ Offsets make_layout(const eagle_config& c) {
   }
   f.orow = L.take(R * 4);
   f.ntile_lm = (V + 63) / 64;
-  f.lm_val = L.take(R * f.ntile_lm * c.topk * 4);
-  f.lm_id = L.take(R * f.ntile_lm * c.topk * 4);
+  f.lm_logits = L.take(static_cast<size_t>(R) * f.ntile_lm * 64 * 4);
   f.lm_stat = L.take(R * f.ntile_lm * 2 * 4);
   f.tk_id = L.take(R * c.topk * 4);
   f.tk_val = L.take(R * c.topk * 4);
@@ -224,8 +223,7 @@ struct Scratch {
   int apack_rows = 0;
   float *at_o = nullptr, *at_ml = nullptr;
   int max_split = 1;
-  float* lm_val = nullptr;
-  int32_t* lm_id = nullptr;
+  float* lm_logits = nullptr;
   float* lm_stat = nullptr;
   int ntile_lm = 0;
 };
@@ -240,7 +238,7 @@ Scratch ctx_scratch(eagle_ctx* c) {
   r.apack = f.apack_rows > 0 ? c->at<char>(f.apack) : nullptr;
   r.apack_rows = f.apack_rows;
   r.at_o = c->at<float>(f.at_o); r.at_ml = c->at<float>(f.at_ml); r.max_split = f.max_split;
-  r.lm_val = c->at<float>(f.lm_val); r.lm_id = c->at<int32_t>(f.lm_id);
+  r.lm_logits = c->at<float>(f.lm_logits);
   r.lm_stat = c->at<float>(f.lm_stat); r.ntile_lm = f.ntile_lm;
   return r;
 }
@@ -437,12 +435,11 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
       return EAGLE_OK;
     }
     p.epi = EPI_LMHEAD;
-    p.cand_val = scr.lm_val; p.cand_id = scr.lm_id;
-    p.stat = scr.lm_stat; p.ntile_lm = scr.ntile_lm; p.topk = cf.topk;
+    p.lm_logits = scr.lm_logits; p.stat = scr.lm_stat; p.ntile_lm = scr.ntile_lm;
     EAGLE_TRY(run_gemm<T>(c, scr, p, s));
     MergeParams m;
-    m.rows = R; m.ntile = scr.ntile_lm; m.topk = cf.topk;
-    m.cand_val = p.cand_val; m.cand_id = p.cand_id; m.stat = p.stat;
+    m.rows = R; m.ntile = scr.ntile_lm; m.topk = cf.topk; m.V = cf.vocab;
+    m.logits = p.lm_logits; m.stat = p.stat;
     m.tok = r.tok; m.out_id = r.topk_id; m.out_val = r.topk_val; m.out_lse = r.lse;
     const int pi = prof_begin(c, PC_MERGE, 0.0, 0.0, s);
     EAGLE_TRY(launch_merge(m, s));

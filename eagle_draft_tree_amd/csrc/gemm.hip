@@ -301,9 +301,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
   const int ntiles = p.N / 16;
   // ---- epilogues -------------------------------------------------------------
   if (p.epi == EPI_LMHEAD) {
-    // the workgroup holds 64 CT consecutive vocabulary columns; stage them in
-    // LDS and emit, per row and per 64-column tile, the top-k candidates and
-    // (max, sum of exp)
+    // the workgroup holds 64 CT consecutive vocabulary columns: stage them in
+    // LDS, store each row's logits, and emit per row and 64-column tile the
+    // (max, sum of exp) that the merge's log-sum-exp and its choice of tiles
+    // need (the merge reads the top-k candidates from the stored logits)
     __syncthreads();
     float* lm = reinterpret_cast<float*>(lds);  // [16 MT rows][64 CT cols]
     constexpr int W = 64 * CT;
@@ -316,55 +317,39 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
           lm[(mt * 16 + 4 * g + j) * W + (wave * CT + ct) * 16 + c] = acc[mt][ct][j];
     __syncthreads();
     const int rows = min(16 * MT, p.M - m0);
+    const int64_t ldl = static_cast<int64_t>(p.ntile_lm) * 64;
     if constexpr (MT == 4) {
-      // many rows: one (row, tile) pair per thread, each keeping its tile's
-      // top-k in registers (a wave-wide sort per pair would take the
-      // workgroup's 64 x CT pairs one at a time per wave); the thread starts
-      // its scan at its own offset, so the threads of a wave read distinct
-      // LDS banks -- the (value, id) order does not depend on scan order
+      // many rows: the logits go out in coalesced row runs, and one thread
+      // per (row, tile) pair takes the pair's max and sum of exp from LDS
+      // (starting at its own offset, so a wave's reads hit distinct banks)
+      for (int idx = threadIdx.x; idx < rows * W; idx += 256) {
+        const int r = idx / W, cw = idx % W;
+        const int col = group * W + cw;
+        if (col >= 64 * p.ntile_lm) continue;
+        float v = col < p.N ? lm[r * W + cw] : -INFINITY;
+        if (v != v) v = -INFINITY;
+        p.lm_logits[(m0 + r) * ldl + col] = v;
+      }
       for (int pr = threadIdx.x; pr < 64 * CT; pr += 256) {
         const int r = pr / CT, ch = pr % CT;
         const int lt = group * CT + ch;
         if (r >= rows || lt >= p.ntile_lm) continue;
-        const float* row = lm + r * W + ch * 64;
-        float lv[kMaxTopK];
-        int li[kMaxTopK];
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+        const float* rowp = lm + r * W + ch * 64;
         float mx = -INFINITY;
         for (int jj = 0; jj < 64; ++jj) {
           const int j = (jj + pr) & 63;
-          const int col = lt * 64 + j;
-          float v = col < p.N ? row[j] : -INFINITY;
+          float v = lt * 64 + j < p.N ? rowp[j] : -INFINITY;
           if (v != v) v = -INFINITY;
-          const int id = col < p.N ? col : 0x7fffffff;
           mx = fmaxf(mx, v);
-          // insertion into the sorted list: slot j takes the new pair when
-          // it beats slot j but not slot j - 1, slot j - 1's pair when the
-          // new one beats that too
-          bool bt[kMaxTopK];
-#pragma unroll
-          for (int k = 0; k < kMaxTopK; ++k) bt[k] = k < p.topk && better(v, id, lv[k], li[k]);
-#pragma unroll
-          for (int k = kMaxTopK - 1; k >= 0; --k) {
-            if (k > 0 && bt[k - 1]) { lv[k] = lv[k - 1]; li[k] = li[k - 1]; }
-            else if (bt[k]) { lv[k] = v; li[k] = id; }
-          }
         }
         float se = 0.f;
         for (int jj = 0; jj < 64; ++jj) {
           const int j = (jj + pr) & 63;
-          float v = lt * 64 + j < p.N ? row[j] : -INFINITY;
+          float v = lt * 64 + j < p.N ? rowp[j] : -INFINITY;
           if (v != v) v = -INFINITY;
           se += v == -INFINITY ? 0.f : expf(v - mx);
         }
         const int64_t o = static_cast<int64_t>(m0 + r) * p.ntile_lm + lt;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-          if (k < p.topk) {
-            p.cand_val[o * p.topk + k] = lv[k];
-            p.cand_id[o * p.topk + k] = li[k];
-          }
         p.stat[o * 2] = mx;
         p.stat[o * 2 + 1] = se;
       }
@@ -376,19 +361,14 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
         const int lt = group * CT + ch;   // 64-column LM tile
         if (lt >= p.ntile_lm) continue;
         const int col = lt * 64 + lane;
+        const int m = m0 + r;
         float v = col < p.N ? lm[r * W + ch * 64 + lane] : -INFINITY;
         if (v != v) v = -INFINITY;
-        int id = col < p.N ? col : 0x7fffffff;
+        p.lm_logits[m * ldl + col] = v;
         const float mx = wave_max(v);
         const float se = wave_sum(v == -INFINITY ? 0.f : expf(v - mx));
-        wave_sort_desc(v, id);
-        const int m = m0 + r;
-        const int64_t o = static_cast<int64_t>(m) * p.ntile_lm + lt;
-        if (lane < p.topk) {
-          p.cand_val[o * p.topk + lane] = v;
-          p.cand_id[o * p.topk + lane] = id;
-        }
         if (lane == 0) {
+          const int64_t o = static_cast<int64_t>(m) * p.ntile_lm + lt;
           p.stat[o * 2] = mx;
           p.stat[o * 2 + 1] = se;
         }

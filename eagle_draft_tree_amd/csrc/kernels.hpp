@@ -72,10 +72,9 @@ struct GemmParams {
   float theta = 10000.f;
   int* status = nullptr;
   // LM-head epilogue
-  float* cand_val = nullptr;      // [M, ntile_lm, topk]
-  int32_t* cand_id = nullptr;
-  float* stat = nullptr;          // [M, ntile_lm, 2]
-  int ntile_lm = 0, topk = 0;
+  float* lm_logits = nullptr;     // [M, 64 ntile_lm] LM-head logits
+  float* stat = nullptr;          // [M, ntile_lm, 2]: per 64-column tile max, sum exp
+  int ntile_lm = 0;
 };
 
 void plan_gemm(GemmParams& p, int num_cus, bool fp32);
@@ -108,10 +107,9 @@ template <typename T> hipError_t launch_attention(const AttnParams& p, hipStream
 
 // LM-head merge, tree growth, verification -----------------------------------
 struct MergeParams {
-  int rows = 0, ntile = 0, topk = 0;
-  const float* cand_val = nullptr;
-  const int32_t* cand_id = nullptr;
-  const float* stat = nullptr;
+  int rows = 0, ntile = 0, topk = 0, V = 0;
+  const float* logits = nullptr;     // [rows, 64 ntile]
+  const float* stat = nullptr;       // [rows, ntile, 2]
   const int32_t* tok = nullptr;      // only rows with tok >= 0 are merged
   int32_t* out_id = nullptr;         // [rows, topk]
   float* out_val = nullptr;          // [rows, topk]

@@ -13,30 +13,28 @@ constexpr int kMaxPath = 72;            // >= D + 1 when (D-1)K <= 64
 // ============================================================================
 // merge: per row, top-k over the LM-head tiles' candidates + log-sum-exp
 // ============================================================================
-// Each 64-column tile of the LM head left its top-k (sorted best-first) and
-// (max, sum of exp).  The row's top-k is found from few of them: with theta
-// the k-th largest tile maximum, k tiles hold an element >= theta, so every
-// element of the row's top-k is >= theta and sits in a tile whose maximum is
-// >= theta, within that tile's own top-k.  Those survivors (a few dozen) are
-// sorted by one wave.  If more than kSurv survive (massive ties), every
-// candidate is scanned instead.
+// The LM head left the row's logits and, per 64-column tile, (max, sum of
+// exp).  The row's top-k is found from few tiles: with theta the k-th
+// largest tile maximum, k tiles hold an element >= theta, so every element of
+// the row's top-k is >= theta and sits in a tile whose maximum is >= theta.
+// Those tiles' elements >= theta (a few dozen) are sorted by one wave.  If
+// more than kSurv survive (massive ties), the whole row is scanned instead.
 constexpr int kSurv = 64;
 
-// Thread-local sorted top-K of this thread's share of all candidates, then
+// Thread-local sorted top-K of this thread's share of the row's logits, then
 // a merge across the workgroup; lane i of wave 0 ends with the i-th best.
-__device__ void merge_all_candidates(const MergeParams& p, int row, float* sv, int* si,
-                                     float& v_out, int& id_out) {
+__device__ void merge_scan_row(const MergeParams& p, int row, float* sv, int* si,
+                               float& v_out, int& id_out) {
   const int K = p.topk;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int64_t base = static_cast<int64_t>(row) * p.ntile;
+  const float* lg = p.logits + static_cast<int64_t>(row) * p.ntile * 64;
   float lv[kMaxTopK];
   int li[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
-  const int ncand = p.ntile * K;
-  for (int idx = threadIdx.x; idx < ncand; idx += 256) {
-    const float v = p.cand_val[base * K + idx];
-    const int id = p.cand_id[base * K + idx];
+  for (int id = threadIdx.x; id < p.V; id += 256) {
+    float v = lg[id];
+    if (v != v) v = -INFINITY;
 #pragma unroll
     for (int j = kMaxTopK - 1; j >= 0; --j) {
       if (j >= K) continue;
@@ -172,27 +170,33 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   __syncthreads();
   const int nt = ntl;
-  if (fast && theta != -INFINITY && nt <= kSurv && nt * K <= 4 * 256) {
-    float cv[4];
-    int ci[4];
+  if (fast && theta != -INFINITY && nt <= kSurv) {
+    // the listed tiles' elements, 16 per thread, all requested before any
+    // is tested (indices clamped into the list)
+    const float* lg = p.logits + static_cast<int64_t>(row) * p.ntile * 64;
+    constexpr int kPer = kSurv * 64 / 256;
+    float cv[kPer];
+    int ci[kPer];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = min(static_cast<int>(threadIdx.x) + 256 * k, nt * K - 1);
-      const int64_t at = (base + stile[idx / K]) * K + idx % K;
-      cv[k] = p.cand_val[at];
-      ci[k] = p.cand_id[at];
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = min(static_cast<int>(threadIdx.x) + 256 * k, nt * 64 - 1);
+      ci[k] = stile[idx >> 6] * 64 + (idx & 63);
+      cv[k] = lg[min(ci[k], p.V - 1)];
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (static_cast<int>(threadIdx.x) + 256 * k < nt * K && cv[k] >= theta) {
+    for (int k = 0; k < kPer; ++k) {
+      float v = cv[k];
+      if (v != v) v = -INFINITY;
+      if (static_cast<int>(threadIdx.x) + 256 * k < nt * 64 && ci[k] < p.V && v >= theta) {
         const int slot = atomicAdd(&nsurv, 1);
         if (slot < kSurv) {
-          sv[slot] = cv[k];
+          sv[slot] = v;
           si[slot] = ci[k];
         }
       }
+    }
   } else if (threadIdx.x == 0) {
-    nsurv = kSurv + 1;   // too many tied tiles: scan every candidate
+    nsurv = kSurv + 1;   // too many tied tiles: scan the whole row
   }
   __syncthreads();
   const int n = nsurv;
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     id = lane < n ? si[lane] : 0x7fffffff;
   } else {
     __syncthreads();
-    merge_all_candidates(p, row, sv, si, v, id);
+    merge_scan_row(p, row, sv, si, v, id);
   }
   if (wave == 0) {
     wave_sort_desc(v, id);

@@ -282,6 +282,8 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
   __shared__ int s_flag[kMaxCand];
   __shared__ int s_scan[256];
   __shared__ int s_prow[128], s_first[128], s_nch[128];
+  __shared__ int s_ntok[kMaxTopK * kMaxTopK], s_nrow[kMaxTopK * kMaxTopK];
+  __shared__ uint64_t s_nmask[kMaxTopK * kMaxTopK];
   const int b = blockIdx.x;
   const int K = p.K, D = p.D, N = p.N;
   const int tid = threadIdx.x;
@@ -344,13 +346,21 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
     const float ps = parent < 0 ? 0.f : ts.c_score[cb + parent];
     float lp = p.topk_val[static_cast<int64_t>(row) * K + cc] - p.lse[row];
     lp = fmaxf(lp, kLogEps);
-    ts.c_token[cb + node] = p.d2t != nullptr ? p.d2t[my] : my;
+    const int tok_out = p.d2t != nullptr ? p.d2t[my] : my;
+    const uint64_t pmask = parent < 0 ? 0ull : ts.c_mask[cb + parent];
+    ts.c_token[cb + node] = tok_out;
     ts.c_parent[cb + node] = parent;
     ts.c_depth[cb + node] = p.pass;
     ts.c_score[cb + node] = ps + lp;
     ts.c_slot[cb + node] = -1;
     ts.c_row[cb + node] = row;
-    ts.c_mask[cb + node] = parent < 0 ? 0ull : ts.c_mask[cb + parent];
+    ts.c_mask[cb + node] = pmask;
+    // the new layer also in LDS, for the expansion below (no reload)
+    const int i = node - first;
+    s_score[i] = ps + lp;
+    s_ntok[i] = tok_out;
+    s_nrow[i] = row;
+    s_nmask[i] = pmask;
   }
   __threadfence_block();
   __syncthreads();
@@ -359,8 +369,6 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
 
   if (!last) {
     // ---- expand the K best of the new layer ----
-    for (int i = tid; i < nnew; i += 256) s_score[i] = ts.c_score[cb + first + i];
-    __syncthreads();
     for (int i = tid; i < nnew; i += 256) {
       int rank = 0;
       const float si = s_score[i];
@@ -374,12 +382,12 @@ __global__ __launch_bounds__(256) void grow_kernel(GrowParams p) {
       for (int j = 0; j < i; ++j) r += s_flag[j];
       const int node = first + i;
       const int slot = (p.pass - 1) * K + r;
-      const uint64_t m = ts.c_mask[cb + node] | (1ull << slot);
+      const uint64_t m = s_nmask[i] | (1ull << slot);
       ts.c_slot[cb + node] = slot;
       ts.c_mask[cb + node] = m;
       const int q = b * K + r;
-      p.nxt.tok[q] = ts.c_token[cb + node];
-      p.nxt.src_row[q] = ts.c_row[cb + node];
+      p.nxt.tok[q] = s_ntok[i];
+      p.nxt.src_row[q] = s_nrow[i];
       p.nxt.pos[q] = p_root + p.pass;
       p.nxt.dest[q] = len_out + slot;
       p.nxt.plen[q] = len_out;

@@ -890,9 +890,9 @@ __global__ __launch_bounds__(256) void pack_a_kernel(GemmParams p) {
   }
 }
 
-template <typename T>
+template <typename T, int CT>
 __global__ __launch_bounds__(256) void dense_gemm_kernel(GemmParams p) {
-  constexpr int MT = 4, CT = 4;
+  constexpr int MT = 4;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1041,15 +1041,20 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
     // round of partial sums through memory, more than a few steps of the
     // main loop): down to about 48 steps per split, while the grid stays
     // within two tiles per CU and the partial sums fit their buffer
-    const int RB = (p.M + 63) / 64, ngroups = (ntiles + 15) / 16;
+    // 64 x 128 tiles (two 16-column tiles per wave) when 64 x 256 ones
+    // would not give every CU two workgroups and K is short enough not to
+    // be split; long K keeps 64 x 256 tiles and is split below
+    const int RB = (p.M + 63) / 64;
     const int ksteps = (p.K + kStep - 1) / kStep;
+    p.MT = 4;
+    p.CT = (ksteps <= 64 && RB * ((ntiles + 15) / 16) < 2 * num_cus) ? 2 : 4;
+    const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
     int S = 1;
     if (ksteps > 64)
       while (ksteps / S > 48 && RB * ngroups * (S + 1) <= 2 * num_cus && S < 16 &&
              static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
         ++S;
     const int steps = (ksteps + S - 1) / S;
-    p.MT = 4; p.CT = 4;
     p.KS = steps * kStep;
     p.S = (ksteps + steps - 1) / steps;
     p.piece_steps = 2;
@@ -1128,6 +1133,24 @@ hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+template <typename T, int CT>
+hipError_t launch_dense_ct(const GemmParams& p, hipStream_t s) {
+  const int RB = (p.M + 63) / 64;
+  const int ngroups = (p.N / 16 + 4 * CT - 1) / (4 * CT);
+  const int ntask = RB * ngroups * p.S;
+  auto kern = dense_gemm_kernel<T, CT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             2 * kDenseABytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((ntask + 7) / 8 * 8), dim3(256), 2 * kDenseABytes, s, p);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_dense(const GemmParams& p, hipStream_t s) {
   if constexpr (sizeof(T) != 2) {
@@ -1136,20 +1159,9 @@ hipError_t launch_dense(const GemmParams& p, hipStream_t s) {
     const int RB = (p.M + 63) / 64;
     const int ksteps = (p.K + kStep - 1) / kStep;
     hipLaunchKernelGGL(pack_a_kernel<T>, dim3(RB, ksteps), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int ngroups = (p.N / 16 + 15) / 16;
-    const int ntask = RB * ngroups * p.S;
-    auto kern = dense_gemm_kernel<T>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kDenseABytes);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3((ntask + 7) / 8 * 8), dim3(256), 2 * kDenseABytes, s, p);
-    return hipGetLastError();
+    return p.CT == 2 ? launch_dense_ct<T, 2>(p, s) : launch_dense_ct<T, 4>(p, s);
   }
 }
 
@@ -1157,7 +1169,8 @@ template <typename T>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.dense) {
     if (p.N % 16 || p.K % 8 || p.K < 8 || p.KS % kStep || p.S < 1 || p.MT != 4 ||
-        p.CT != 4 || static_cast<int64_t>(p.S) * p.KS < p.K || p.M > p.apack_rows ||
+        (p.CT != 4 && p.CT != 2) || static_cast<int64_t>(p.S) * p.KS < p.K ||
+        p.M > p.apack_rows ||
         (p.S > 1 && (p.part == nullptr || p.cnt == nullptr ||
                      static_cast<int64_t>(p.S) * p.Mtot * p.N > p.part_elems)) ||
         p.wpack == nullptr || p.apack == nullptr)

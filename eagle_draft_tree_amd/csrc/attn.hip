@@ -169,10 +169,9 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   };
 
   // ---- staging: thread t moves 16-byte chunks t + 256 i of a step ----
-  u32x4 stg[L::CPT];
   // request the chunks of the step at t0 (rows past the cache read its last
   // rows; dead keys are masked when the step is used)
-  auto fetch = [&](int t0) {
+  auto fetch = [&](int t0, u32x4 (&stg)[L::CPT]) {
 #pragma unroll
     for (int i = 0; i < L::CPT; ++i) {
       const int q = tid + 256 * i;
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       }
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&](const u32x4 (&stg)[L::CPT], int buf) {
     unsigned char* base = lds + buf * L::BUF;
 #pragma unroll
     for (int i = 0; i < L::CPT; ++i) {
@@ -317,17 +316,40 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     }
   };
 
-  // ---- the steps: step s + 1 is staged from registers while step s is
-  // used, and the loads of step s + 2 are in flight meanwhile ----
+  // ---- the steps ----
   const int nst = kbeg < kend ? (kend - kbeg + 31) / 32 : 0;
-  if (nst > 0) {
-    fetch(kbeg);
-    put(0);
-    if (nst > 1) fetch(kbeg + 32);
+  if (nst > 0 && !scratch) {
+    // prefix keys: step s + 1 is staged from registers while step s is used,
+    // the loads of steps s + 2 and s + 3 in flight meanwhile (two register
+    // sets).  Every fetch is issued, past the range re-reading the last
+    // step, so that each wait counts the same loads behind it.
+    u32x4 r0[L::CPT], r1[L::CPT];
+    auto step_t0 = [&](int st) { return kbeg + 32 * min(st, nst - 1); };
+    fetch(step_t0(0), r0);
+    put(r0, 0);
+    fetch(step_t0(1), r0);
+    fetch(step_t0(2), r1);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+      put(r0, 1);                        // step st + 1
+      fetch(step_t0(st + 3), r0);
+      if (active) compute(kbeg + 32 * st, 0);
+      __syncthreads();
+      if (st + 1 >= nst) break;
+      put(r1, 0);                        // step st + 2
+      fetch(step_t0(st + 4), r1);
+      if (active) compute(kbeg + 32 * (st + 1), 1);
+      __syncthreads();
+    }
+  } else if (nst > 0) {
+    // the tree's own rows (at most two steps): one register set
+    u32x4 r0[L::CPT];
+    fetch(kbeg, r0);
+    put(r0, 0);
+    if (nst > 1) fetch(kbeg + 32, r0);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) put((st + 1) & 1);
-      if (st + 2 < nst) fetch(kbeg + 32 * (st + 2));
+      if (st + 1 < nst) put(r0, (st + 1) & 1);
       if (active) compute(kbeg + 32 * st, st & 1);
       __syncthreads();
     }

@@ -403,7 +403,7 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
     p.ss = scr.ss;
     EAGLE_TRY(run_gemm<T>(c, scr, p, s));
   }
-  // a7 final norm -> LM head -> per-tile top-k -> merge (or every logit)
+  // a7 final norm -> LM head (logits + per-tile max / sum exp) -> merge (or every logit)
   {
     GemmParams p;
     c->shape(G_LM, p);

@@ -4,9 +4,10 @@
 //  * a workgroup owns 64 CT output columns (four waves of CT 16-column tiles)
 //    and one slice of K (S slices split K across workgroups);
 //  * its slice of A is normalised (RMSNorm factor and gain), split into
-//    bf16 hi + lo parts and laid out in LDS in MFMA fragment order once, at
-//    the start -- every wave then reads its A fragments with one 16-byte LDS
-//    load per MFMA;
+//    bf16 hi + lo parts and laid out in LDS in MFMA fragment order, one
+//    piece of steps at a time, the next piece fetched into registers while
+//    the current one is used -- every wave then reads its A fragments with
+//    one 16-byte LDS load per MFMA;
 //  * the weights are packed once (pack_weights) in MFMA fragment order: for
 //    each 128-wide k step, 16-column tile and 32-wide sub-step e, the 64
 //    lanes' 8-element fragments lie contiguously, so every weight load of a

@@ -66,7 +66,7 @@ def _stream():
 class KVCache:
     """Draft KV cache: k [B, n_kv, cap, hd] (key rows), v [B, n_kv, hd, cap]
     (values stored transposed), committed lengths [B] (int32); cap is a
-    multiple of 8."""
+    multiple of 8 and at least 32."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, length: torch.Tensor):
         assert k.dim() == 4 and v.dim() == 4 and k.is_contiguous() and v.is_contiguous()

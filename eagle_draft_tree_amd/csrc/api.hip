@@ -655,6 +655,10 @@ bool null_tree(const eagle_tree* t) {
          !t->n_nodes;
 }
 
+// A draft KV cache holds whole 16-byte runs of keys (cap a multiple of 8)
+// and at least one 32-key attention step.
+bool bad_draft_cap(int32_t cap) { return cap < 32 || cap % 8 != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -805,7 +809,7 @@ eagle_status eagle_draft_step(eagle_ctx* ctx, int32_t batch, int32_t rows_per_se
       rows_per_seq > std::max(cf.max_seed, cf.topk))
     return EAGLE_EINVAL;
   if (!src || !token || !position || !dest || !prefix_len || !scratch_base ||
-      !scratch_mask || !kv->k || !kv->v || kv->cap < 8 || kv->cap % 8 || !a_out || !topk_id ||
+      !scratch_mask || !kv->k || !kv->v || bad_draft_cap(kv->cap) || !a_out || !topk_id ||
       !topk_logit || !lse)
     return EAGLE_EINVAL;
   Rows r;
@@ -825,7 +829,7 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, int32_t batch, const void* seed_sr
   const eagle_config& cf = ctx->cfg;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
   if (!seed_src || !seed_token || !seed_len || !kv->k || !kv->v || !kv->len_in ||
-      !kv->len_out || kv->cap < 8 || kv->cap % 8)
+      !kv->len_out || bad_draft_cap(kv->cap))
     return EAGLE_EINVAL;
   return cf.dtype == EAGLE_BF16
              ? draft_tree_impl<uint16_t>(ctx, batch, seed_src, seed_token, seed_len, kv,
@@ -844,7 +848,7 @@ eagle_status eagle_draft_tree_sampled(eagle_ctx* ctx, int32_t batch, const void*
   const eagle_config& cf = ctx->cfg;
   if (batch < 1 || batch > cf.max_batch) return EAGLE_EINVAL;
   if (!seed_src || !seed_token || !seed_len || !kv->k || !kv->v || !kv->len_in ||
-      !kv->len_out || kv->cap < 8 || kv->cap % 8)
+      !kv->len_out || bad_draft_cap(kv->cap))
     return EAGLE_EINVAL;
   if (!(temperature > 0.f) || !std::isfinite(temperature)) return EAGLE_EINVAL;
   // every draw stays in the tree, in draw order; one vocabulary
@@ -892,7 +896,7 @@ eagle_status verify_core(const eagle_config& cf, const VerifyScratch& ws, eagle_
   if (cf.max_seed < (commit_mode == EAGLE_COMMIT_RESEED ? cf.depth + 1 : 2))
     return EAGLE_EUNSUPPORTED;
   if (kv_or_null && (!kv_or_null->k || !kv_or_null->v || !kv_or_null->len_out ||
-                     kv_or_null->cap < 8 || kv_or_null->cap % 8))
+                     bad_draft_cap(kv_or_null->cap)))
     return EAGLE_EINVAL;
   VerifyParams p;
   p.batch = batch; p.N = cf.budget; p.K = cf.topk; p.D = cf.depth; p.V = tvocab(cf);

@@ -266,9 +266,13 @@ __device__ __forceinline__ void qkv_element(const GemmParams& p, int m, int col,
   const int hh = col / p.hd, cin = col % p.hd;
   float y = x;
   if (hh < p.nq + p.nkv) {
-    double sd, cd;
-    sincos(static_cast<double>(p.pos[m]) * inv, &sd, &cd);
-    const float cs = static_cast<float>(cd), sn = static_cast<float>(sd);
+    // the angle in double (at positions in the thousands a float product is
+    // off by 1e-3 rad and more), reduced there to [-pi, pi]; its sine and
+    // cosine then in float, within a few 1e-7 of the exact ones
+    const double a = static_cast<double>(p.pos[m]) * inv;
+    const double red = a - rint(a * 0.15915494309189535) * 6.283185307179586;
+    float sn, cs;
+    sincosf(static_cast<float>(red), &sn, &cs);
     y = (c < 8) ? (x * cs - other * sn) : (x * cs + other * sn);
   }
   const T v = Elem<T>::from_f(y);
@@ -380,8 +384,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4 (&acc)[MT][C
 
   if (p.epi == EPI_QKV) {
     // values and RoPE partners first, in a loop small enough to unroll;
-    // then the element work, whose double-precision sincos would keep a
-    // loop over the accumulators from unrolling (and put them in scratch)
+    // then the element work, whose calls (pow, sincos) would keep a loop
+    // over the accumulators from unrolling (and put them in scratch)
     float xs[CT][4 * MT], os[CT][4 * MT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -1028,9 +1032,9 @@ template hipError_t launch_pack<float>(const GemmParams&, void*, hipStream_t);
 namespace {
 
 size_t lds_bytes(int MT, int steps) { return static_cast<size_t>(steps * 4 * MT + 1) * kBlk; }
-// most k steps of A one LDS piece holds: 8 / 4 / 4 for 1 / 2 / 4 row tiles
-// (66 KB, 66 KB and 130 KB of LDS)
-int max_piece(int MT) { return MT == 1 ? 8 : 4; }
+// most k steps of A one LDS piece holds (34 KB, 66 KB and 130 KB of LDS for
+// 1, 2 and 4 row tiles): longer pieces measured slower at one row tile
+constexpr int kMaxPiece = 4;
 
 }  // namespace
 
@@ -1069,7 +1073,6 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   p.CT = (!fp32 && ntiles >= 16 * num_cus) ? 2 : 1;
   const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
   const int ksteps = (p.K + kStep - 1) / kStep;
-  const int pmax = max_piece(p.MT);
   // no K split when the column groups alone cover every CU; else split K
   // until the grid holds about one workgroup per CU (each split's partial
   // sums cost a round trip through memory, so fewer, longer splits do
@@ -1077,17 +1080,21 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   int S = 1;
   if (ngroups * chunks < num_cus)
     while (ngroups * chunks * S < num_cus && (ksteps + S) / (S + 1) >= 2 && S < 16) ++S;
+  // a grid a little over one workgroup per CU keeps most CUs idle while the
+  // excess runs: one split fewer when that still covers 3/4 of the CUs
+  const int tiles_s = ngroups * chunks;
+  if (S > 1 && tiles_s * S > num_cus && 4 * tiles_s * (S - 1) >= 3 * num_cus) --S;
   // the partial sums must fit the workspace
   while (S > 1 && static_cast<int64_t>(S) * p.Mtot * p.N > p.part_elems) --S;
   // a split longer than 4 steps is rounded up to whole pieces (fewer,
   // longer splits): steps past the slice still stream their weights, against
   // zero A, so a ragged piece costs bandwidth
   int steps = (ksteps + S - 1) / S;
-  if (steps > 4) steps = (steps + pmax - 1) / pmax * pmax;
+  if (steps > kMaxPiece) steps = (steps + kMaxPiece - 1) / kMaxPiece * kMaxPiece;
   p.KS = steps * kStep;
   p.S = (ksteps + steps - 1) / steps;
   // smallest unrolled piece that holds the slice (several pieces otherwise)
-  p.piece_steps = steps <= 2 ? 2 : (steps <= 4 ? 4 : pmax);
+  p.piece_steps = steps <= 2 ? 2 : kMaxPiece;
 }
 
 namespace {
@@ -1117,10 +1124,8 @@ template <typename T, int MT, int CT>
 hipError_t launch_ps(const GemmParams& p, hipStream_t s) {
   switch (p.piece_steps) {
     case 2: return launch_one<T, MT, CT, 2>(p, s);
-    case 4: return launch_one<T, MT, CT, 4>(p, s);
-    default:
-      if constexpr (MT == 1) return launch_one<T, MT, CT, 8>(p, s);
-      return hipErrorInvalidValue;
+    case kMaxPiece: return launch_one<T, MT, CT, kMaxPiece>(p, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -1183,7 +1188,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       (p.S > 1 && (p.part == nullptr || p.cnt == nullptr)) ||
       (p.CT == 2 && sizeof(T) != 2) || p.wpack == nullptr)
     return hipErrorInvalidValue;
-  // a split either fits one piece or spans whole pieces of 4 or 8 steps
+  // a split either fits one piece or spans whole pieces of kMaxPiece steps
   if (p.KS / kStep > p.piece_steps && p.piece_steps < 4) return hipErrorInvalidValue;
   switch (p.MT) {
     case 1: return launch_mt<T, 1>(p, s);

@@ -119,9 +119,9 @@ typedef struct {
  * separate from the target's), config dtype: k [B, n_kv, cap, hd] (row r of
  * a head is key r) and v [B, n_kv, hd, cap] (stored transposed: column r of
  * a head is value r), so that tree attention reads both as matrix-core
- * operands directly.  cap is a multiple of 8.  Rows [0, len) are committed;
- * a draft call appends its seed rows there and uses rows
- * [len_out, len_out + (D-1)K) as tree scratch.  len_in is read, len_out
+ * operands directly.  cap is a multiple of 8 and at least 32 (else EINVAL).
+ * Rows [0, len) are committed; a draft call appends its seed rows there and
+ * uses rows [len_out, len_out + (D-1)K) as tree scratch.  len_in is read, len_out
  * written, so a call can be replayed with the same inputs. */
 
 typedef struct {

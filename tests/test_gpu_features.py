@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import synth
-from harness import SEED, Model, first_round, run_chain, stored
+from harness import SEED, Model, first_round, run_chain, stored, tdtype
 
 pytestmark = pytest.mark.gpu
 
@@ -114,3 +114,25 @@ def test_reduced_draft_vocabulary():
                    d2t=d2t, TV=TV)
     finally:
         m.gpu.pop("d2t")
+
+
+def test_draft_cache_capacity_rule():
+    """A draft cache must hold at least one 32-key attention step in whole
+    16-byte runs (cap a multiple of 8, at least 32): smaller or ragged
+    capacities are rejected before anything is launched."""
+    from eagle_draft_tree_amd import KVCache
+    from eagle_draft_tree_amd._lib import EagleError
+    m = _model("chain", synth.config("8b_bs1", **MID, K=1, D=3, N=3))
+    cfg = m.cfg
+    d = m.drafter(max_batch=1)
+    S = d.shape.max_seed
+    seed_src = torch.zeros(1, S, cfg.H, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, S, dtype=torch.int32, device="cuda")
+    seed_len = torch.ones(1, dtype=torch.int32, device="cuda")
+    for cap in (24, 36):
+        k = torch.zeros(1, cfg.n_kv, cap, cfg.hd, dtype=tdtype(cfg), device="cuda")
+        kv = KVCache.from_rows(k, k.clone(), torch.zeros(1, dtype=torch.int32, device="cuda"))
+        with pytest.raises(EagleError) as e:
+            d.draft_tree(seed_src, tok, seed_len, kv)
+        assert e.value.code == 1  # invalid argument
+    print("[cap] capacities 24 and 36 rejected", flush=True)

@@ -1042,21 +1042,23 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int ntiles = p.N / 16;
   p.dense = !fp32 && p.M > 64 && p.apack != nullptr && p.M <= p.apack_rows;
   if (p.dense) {
-    // 64 x 256 tiles; K is split only when it is long (a split costs a
-    // round of partial sums through memory, more than a few steps of the
-    // main loop): down to about 48 steps per split, while the grid stays
-    // within two tiles per CU and the partial sums fit their buffer
-    // 64 x 128 tiles (two 16-column tiles per wave) when 64 x 256 ones
-    // would not give every CU two workgroups and K is short enough not to
-    // be split; long K keeps 64 x 256 tiles and is split below
+    // 64 x 256 tiles (four 16-column tiles per wave).  K is split only when
+    // it is long (64 steps and more; a split costs a round of partial sums
+    // through memory, more than a few steps of the main loop): into as many
+    // splits of at least 8 steps as keep the grid within two tiles per CU and
+    // the partial sums within their buffer.  Shorter K is not split, and
+    // takes 64 x 128 tiles when 64 x 256 ones would not give every CU two
+    // workgroups (measured: 64 x 256 tiles with split K do better for long K,
+    // worse for short K, where the split's partial sums weigh more)
     const int RB = (p.M + 63) / 64;
     const int ksteps = (p.K + kStep - 1) / kStep;
+    const bool longk = ksteps >= 64;
     p.MT = 4;
-    p.CT = (ksteps <= 64 && RB * ((ntiles + 15) / 16) < 2 * num_cus) ? 2 : 4;
+    p.CT = (!longk && RB * ((ntiles + 15) / 16) < 2 * num_cus) ? 2 : 4;
     const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
     int S = 1;
-    if (ksteps > 64)
-      while (ksteps / S > 48 && RB * ngroups * (S + 1) <= 2 * num_cus && S < 16 &&
+    if (longk)
+      while (ksteps / (S + 1) >= 8 && RB * ngroups * (S + 1) <= 2 * num_cus && S < 16 &&
              static_cast<int64_t>(S + 1) * p.Mtot * p.N <= p.part_elems)
         ++S;
     const int steps = (ksteps + S - 1) / S;

@@ -77,7 +77,7 @@ struct AttnTile {
 };
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 3) void tree_attn_kernel(AttnParams p) {
   using L = AttnTile<T, HD>;
   constexpr int NE = HD / 32;   // 8-element fragments per lane per query / key
   constexpr int NB = HD / 16;   // 16-dim blocks of O^T
@@ -228,35 +228,17 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   auto compute = [&](int t0, int buf) {
     const unsigned char* kt = lds + buf * L::BUF;
     const unsigned char* vtt = kt + 32 * L::KSTR;
-    Frag8<T> kf[2][NE];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < NE; ++e)
-        lds_frag8<T>(kt + (kb * 16 + c) * L::KSTR + (g * (HD / 4) + 8 * e) * sizeof(T), kf[kb][e]);
-    Frag8<T> vf[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const unsigned char* vr = vtt + (nb * 16 + c) * L::VSTR;
-      lds_half4<T>(vr + 4 * g * sizeof(T), vf[nb], 0);
-      lds_half4<T>(vr + (16 + 4 * g) * sizeof(T), vf[nb], 1);
-    }
-    // dead keys' V is zero (their probabilities are zero, and the rows they
-    // were read from may hold anything); a step of live keys skips this
-    if (!(t0 + 32 <= kend && !scratch)) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8)
-          if (!key_live(t0, 16 * (e8 >> 2) + 4 * g + (e8 & 3))) vf[nb].set(e8, 0.f);
-    }
-    // S^T block: 32 keys x 16 query columns
+    // S^T block: 32 keys x 16 query columns, one 16-key half at a time
     f32x4 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      Frag8<T> kf[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+        lds_frag8<T>(kt + (kb * 16 + c) * L::KSTR + (g * (HD / 4) + 8 * e) * sizeof(T), kf[e]);
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < NE; ++e) sc[kb] = mfma16(kf[kb][e], qf[e], sc[kb]);
+      for (int e = 0; e < NE; ++e) sc[kb] = mfma16(kf[e], qf[e], sc[kb]);
     }
     float tmax = -INFINITY;
 #pragma unroll
@@ -309,10 +291,34 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
         pl.set(4 + i, p1 - ph.get(4 + i));
       }
     }
+    // O^T += V^T P^T, half of the 16-dim blocks at a time (the V^T
+    // fragments are read only now, and half of them at once: fewer registers
+    // live, three waves per SIMD).  Dead keys' V is zero (their
+    // probabilities are zero, and the rows they were read from may hold
+    // anything); a step of live prefix keys skips that.
+    const bool all_live = t0 + 32 <= kend && !scratch;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      oacc[nb] = mfma16(vf[nb], ph, oacc[nb]);
-      if constexpr (sizeof(T) == 2) oacc[nb] = mfma16(vf[nb], pl, oacc[nb]);
+    for (int h = 0; h < 2; ++h) {
+      Frag8<T> vf[NB / 2];
+#pragma unroll
+      for (int i = 0; i < NB / 2; ++i) {
+        const unsigned char* vr = vtt + ((h * NB / 2 + i) * 16 + c) * L::VSTR;
+        lds_half4<T>(vr + 4 * g * sizeof(T), vf[i], 0);
+        lds_half4<T>(vr + (16 + 4 * g) * sizeof(T), vf[i], 1);
+      }
+      if (!all_live) {
+#pragma unroll
+        for (int i = 0; i < NB / 2; ++i)
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8)
+            if (!key_live(t0, 16 * (e8 >> 2) + 4 * g + (e8 & 3))) vf[i].set(e8, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < NB / 2; ++i) {
+        const int nb = h * NB / 2 + i;
+        oacc[nb] = mfma16(vf[i], ph, oacc[nb]);
+        if constexpr (sizeof(T) == 2) oacc[nb] = mfma16(vf[i], pl, oacc[nb]);
+      }
     }
   };
 

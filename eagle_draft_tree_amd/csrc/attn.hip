@@ -76,6 +76,8 @@ struct AttnTile {
   static_assert(NKC % 256 == 0 && NCH % 256 == 0, "chunks split evenly over 256 threads");
 };
 
+// Three workgroups per CU (the second launch bound): at most 168 registers per
+// lane, which the fragment order in `compute` below meets without spilling.
 template <typename T, int HD>
 __global__ __launch_bounds__(256, 3) void tree_attn_kernel(AttnParams p) {
   using L = AttnTile<T, HD>;

@@ -356,12 +356,17 @@ eagle_status run_block(eagle_ctx* c, const Scratch& scr, const Rows& r, const ea
     p.kc = kv->k; p.vc = kv->v; p.tok = r.tok; p.plen = r.plen;
     p.sbase = r.sbase; p.smask = r.mask;
     // splits: about 2048 workgroups over the batch (each stages 32-key
-    // steps of K and V for up to four 16-query blocks), at least 64 keys each
+    // steps of K and V for up to four 16-query blocks), at least 128 keys
+    // each (shorter splits cost more in the merge than they save: 3 us per
+    // pass at one sequence of 2048 keys)
+    constexpr int kMinSplitKeys = 128;
     const int G = cf.n_q_heads / cf.n_kv_heads;
     const int nrounds = ((r.rps * G + 15) / 16 + 3) / 4;
     const int want = std::max(1, 2048 / std::max(1, r.batch * cf.n_kv_heads * nrounds));
-    int nsplit = std::min({scr.max_split, std::max(1, (kv->cap + 63) / 64), want});
-    const int split_keys = std::max(64, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);
+    int nsplit = std::min(
+        {scr.max_split, std::max(1, (kv->cap + kMinSplitKeys - 1) / kMinSplitKeys), want});
+    const int split_keys =
+        std::max(kMinSplitKeys, ((kv->cap + nsplit - 1) / nsplit + 63) / 64 * 64);
     nsplit = (kv->cap + split_keys - 1) / split_keys;
     p.nsplit = nsplit; p.split_keys = split_keys;
     p.part_o = scr.at_o; p.part_ml = scr.at_ml;

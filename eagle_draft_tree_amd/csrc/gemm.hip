@@ -1070,9 +1070,15 @@ void plan_gemm(GemmParams& p, int num_cus, bool fp32) {
   const int rows = p.M < 64 ? p.M : 64;
   p.MT = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   const int chunks = (p.M + 16 * p.MT - 1) / (16 * p.MT);
-  // one 16-column tile per wave; two only when there are far more tiles
-  // than the chip holds (bf16 only: fp32 fragments take twice the registers)
-  p.CT = (!fp32 && ntiles >= 16 * num_cus) ? 2 : 1;
+  // one 16-column tile per wave; two (bf16 only: fp32 fragments take twice
+  // the registers) when there are far more tiles than the chip holds, and
+  // for the wide gate/up product at one row tile: at 8B (1792 tiles) it
+  // streams 5% faster as 224 workgroups of two tiles per wave than as 448 of
+  // one.  Measured no gain for the LM head (2000 tiles), and a 20% loss for
+  // the narrower products, which then need more K splits.
+  p.CT = (!fp32 && (ntiles >= 16 * num_cus ||
+                    (p.M <= 16 && ntiles >= 4 * num_cus && p.epi == EPI_SWIGLU)))
+             ? 2 : 1;
   const int ngroups = (ntiles + 4 * p.CT - 1) / (4 * p.CT);
   const int ksteps = (p.K + kStep - 1) / kStep;
   // no K split when the column groups alone cover every CU; else split K

@@ -15,6 +15,21 @@ import synth
 MARGIN = 1e-3
 
 
+# Progress lines reach the terminal even while pytest captures output: the
+# full-shape tests spend minutes in the oracle between results, and a run that
+# prints nothing for that long looks hung.  The capture manager is set by
+# those tests' fixture; elsewhere say() is a plain print.
+_capman = None
+
+
+def say(msg: str) -> None:
+    if _capman is not None:
+        with _capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+    else:
+        print(msg, flush=True)
+
+
 def tol(cfg):
     return (2e-2, 2e-2) if cfg.dtype == "bf16" else (1e-4, 1e-4)
 
@@ -263,7 +278,7 @@ def first_round(m, B, cap_rounds=1, d2t=None, s_max=None, check=None, **shape_kw
         on = check is None or b in check
         seqs.append(make_seq(m, b, int(ctxs[b]), cap, run_oracle=on, d2t=d2t))
         if on:
-            print(f"[oracle] sequence {b} ctx {int(ctxs[b])} tree built", flush=True)
+            say(f"[oracle] sequence {b} ctx {int(ctxs[b])} tree built")
     d = m.drafter(max_batch=B, **({"max_seed": s_max} if s_max else {}), **shape_kw)
     kv, feats, tok, seed_len = upload_batch(m, seqs, cap, s_max=d.shape.max_seed)
     g, tree, len_out = gpu_tree_round(d, m, seqs, kv, feats, tok, seed_len)
@@ -326,6 +341,5 @@ def run_chain(m, seqs, d, kv, tree, rounds, T, mode, d2t=None, TV=None):
         for b, c in enumerate(chains):
             assert int(len_out[b]) == c.len_out
             assert_tree_equal(cfg, tree_to_np(tree, b), c.tree)
-        print(f"[chain] round {rnd + 1} trees equal (attempts {atts})", flush=True)
-    print(f"[chain] T={T} mode={mode}: accepted {accepted} over {rounds} rounds",
-          flush=True)
+        say(f"[chain] round {rnd + 1} trees equal (attempts {atts})")
+    say(f"[chain] T={T} mode={mode}: accepted {accepted} over {rounds} rounds")

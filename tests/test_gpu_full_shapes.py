@@ -21,12 +21,22 @@ import numpy as np
 import pytest
 import torch
 
+import harness
 import synth
-from harness import SEED, Model, first_round, run_chain, tree_to_np, assert_tree_equal
+from harness import SEED, Model, first_round, run_chain, say, tree_to_np, assert_tree_equal
 
 pytestmark = pytest.mark.gpu
 
 _held = {}
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _progress_to_terminal(pytestconfig):
+    """These tests run for minutes, mostly in the oracle: their progress
+    lines bypass pytest's output capture."""
+    harness._capman = pytestconfig.pluginmanager.getplugin("capturemanager")
+    yield
+    harness._capman = None
 
 
 def _dims(cfg):
@@ -43,7 +53,7 @@ def _model(name):
         _held.clear()
         gc.collect()
         torch.cuda.empty_cache()
-        print(f"[setup] weights for {name}", flush=True)
+        say(f"[setup] weights for {name}")
         base = _held["base"] = Model(cfg)
     m = copy.copy(base)
     m.cfg = cfg
@@ -55,14 +65,14 @@ def _model(name):
 def test_8b_bs1_two_rounds_greedy():
     m = _model("8b_bs1")
     seqs, d, kv, tree = first_round(m, 1, cap_rounds=3)
-    print("[8b bs1] first tree equal", flush=True)
+    say("[8b bs1] first tree equal")
     run_chain(m, seqs, d, kv, tree, rounds=2, T=0.0, mode="keep")
 
 
 def test_8b_bs64_sampling_every_sequence():
     m = _model("8b_bs64")
     seqs, d, kv, tree = first_round(m, 64)
-    print("[8b bs64] 64 trees equal", flush=True)
+    say("[8b bs64] 64 trees equal")
     run_chain(m, seqs, d, kv, tree, rounds=1, T=1.0, mode="keep")
 
 
@@ -71,14 +81,14 @@ def test_long_context_bs8_four_chained_rounds():
     seqs, d, kv, tree = first_round(m, 8, cap_rounds=5)
     for b in range(8):
         assert_tree_equal(m.cfg, tree_to_np(tree, b), seqs[b].tree)
-    print("[long bs8] 8 trees equal (two mask words per row)", flush=True)
+    say("[long bs8] 8 trees equal (two mask words per row)")
     run_chain(m, seqs, d, kv, tree, rounds=4, T=0.6, mode="keep")
 
 
 def test_70b_bs1_greedy():
     m = _model("70b_bs1")
     seqs, d, kv, tree = first_round(m, 1, cap_rounds=2)
-    print("[70b bs1] tree equal", flush=True)
+    say("[70b bs1] tree equal")
     run_chain(m, seqs, d, kv, tree, rounds=1, T=0.0, mode="keep")
 
 
@@ -88,7 +98,7 @@ def test_70b_bs16_subset_sampling():
     m = _model("70b_bs1")
     check = (0, 7, 15)
     seqs, d, kv, tree = first_round(m, 16, check=check)
-    print("[70b bs16] checked trees equal", flush=True)
+    say("[70b bs16] checked trees equal")
     from harness import ChainSeq, as_np, close
     from eagle_draft_tree_amd import COMMIT_KEEP
     cfg = m.cfg
